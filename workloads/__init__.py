@@ -1,0 +1,30 @@
+"""Seeded synthetic inputs shared by the oracle-side tests and the GPU path.
+
+This module draws random numbers, rounds them to the storage formats and lays
+them out in the cache formats.  It holds none of the attention or projection
+arithmetic.
+"""
+
+from .gen import (
+    DecodeCase,
+    QueryInputs,
+    bf16_round_bits,
+    config_case,
+    config_query_inputs,
+    make_decode_case,
+    make_query_inputs,
+    ragged_lengths,
+    CONFIG_NAMES,
+)
+
+__all__ = [
+    "DecodeCase",
+    "QueryInputs",
+    "bf16_round_bits",
+    "config_case",
+    "config_query_inputs",
+    "make_decode_case",
+    "make_query_inputs",
+    "ragged_lengths",
+    "CONFIG_NAMES",
+]
