@@ -1,0 +1,195 @@
+"""Benchmark of the MFA decode-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--pools P]
+
+A step is one decode-attention call (block-table walk, K/V tile loads,
+QK^T and PV on MFMA, online softmax, split combine) over one batch of
+synthetic input already resident in HBM.  Default workload: 64 slots x 4096
+keys, 64 query heads sharing one 256-wide K/V head, bf16, paged 64-token
+blocks in a shuffled pool.  The K/V pool is replicated P times and the steps
+rotate through the copies so that the 256 MB Infinity Cache cannot serve a
+repeat of the previous step.  Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn query tokens/s + achieved HBM GB/s (% peak), MFA 4K ctx, batch 64"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+WORKLOADS = {
+    2: "MFA decode: B=64, every context 4096, 64 q heads / 1 KV head, d=256, bf16 q/K/V, "
+       "paged 64-token blocks, shuffled pool",
+    3: "MFA decode: B=128 ragged (prefill U[1024,8192] + Geo(1/1024) decode index), bf16, paged",
+    4: "MFA decode: B=256, context 4096, FP8 E4M3 K/V with per-head scales, bf16 q, paged",
+    5: "GQA 64/4/192 decode: B=32, context 32768, dense global layer, bf16, paged",
+    6: "GQA 64/4/192 decode: B=32, context 32768, 512-token sliding window, bf16, paged",
+}
+
+
+def make_case(config):
+    from workloads import config_case
+    if config in (2, 3, 4):
+        return config_case(config, nan_tail=False)
+    if config == 5:
+        return config_case(5, window=0, nan_tail=False)
+    if config == 6:
+        return config_case(5, window=512, nan_tail=False)
+    raise SystemExit(f"unknown --config {config}")
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle as it stands, on the host cores, over as many slots of the
+    same workload as fit in about budget_s seconds."""
+    from threadpoolctl import threadpool_info
+    from oracle import decode_attention
+    q = case.q
+    if q is None:   # FP8 config: q comes from the query path; time attention on a drawn q
+        from workloads import bf16_round_bits
+        rng = np.random.default_rng(404)
+        q = bf16_round_bits(rng.standard_normal((case.batch, case.hq, case.d), dtype=np.float32))
+    kw = case.oracle_kwargs()
+    done = 0
+    t0 = time.perf_counter()
+    while done < case.batch and (time.perf_counter() - t0) < budget_s:
+        decode_attention(q, case.k_cache, case.v_cache, case.ctx_lens, case.scale,
+                         slots=[done], **kw)
+        done += 1
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": done / el, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {case.batch} slots of the same workload ({case.name}), "
+                      f"fp64 numpy oracle, {el:.1f} s",
+            "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--pools", type=int, default=4)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the decode path shards by slot with no cross-GPU traffic, so run one "
+              "process per GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_mfa_amd as mfa
+    from decode_attention_mfa_amd import accounting
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import to_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: building config {args.config} inputs")
+    case = make_case(args.config)
+    t = to_device(case, device=dev)
+    if t["q"] is None:   # FP8 config without the query path: draw q (bf16) on the host
+        from workloads import bf16_round_bits
+        rng = np.random.default_rng(404)
+        qh = bf16_round_bits(rng.standard_normal((case.batch, case.hq, case.d), dtype=np.float32))
+        t["q"] = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
+    pools = [(t["k"], t["v"])]
+    for _ in range(max(0, args.pools - 1)):
+        pools.append((t["k"].clone(), t["v"].clone()))
+    out = t["out"]
+    window = case.window
+
+    def call(i):
+        k, v = pools[i % len(pools)]
+        if case.hkv == 1 and window == 0:
+            mfa.mfa_decode_attention(t["q"], k, v, t["table"], t["lens"], out, case.scale,
+                                     k_scale=t["k_scale"], v_scale=t["v_scale"],
+                                     num_splits=args.num_splits)
+        else:
+            mfa.mfa_decode_attention_gqa(t["q"], k, v, t["table"], t["lens"], out, case.scale,
+                                         window=window, k_scale=t["k_scale"],
+                                         v_scale=t["v_scale"], num_splits=args.num_splits)
+
+    log(f"bench: warmup {args.warmup}")
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean(per_call_ms))
+
+    fmt_kv = case.kv_format
+    nbytes = accounting.decode_call_bytes(case.ctx_lens, hq=case.hq, hkv=case.hkv, d=case.d,
+                                          q_fmt="bf16", kv_fmt=fmt_kv, out_fmt=case.out_format,
+                                          window=window)
+    flops = accounting.decode_call_flops(case.ctx_lens, hq=case.hq, d=case.d, window=window)
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    desc = mfa.decode_desc(t["q"], t["k"], t["table"], out, args.num_splits)
+    splits = mfa.mfa_decode_plan_splits(desc, window,
+                                        torch.cuda.get_device_properties(dev).multi_processor_count)
+
+    res = {
+        "metric": METRIC,
+        "value": case.batch / (ms_per_step * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "e4m3": "fp8_e4m3 storage, bf16 MFMA", "f32": "f32"}[fmt_kv],
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "batch": case.batch,
+                   "ctx_len_mean": float(np.mean(case.ctx_lens)), "q_heads": case.hq,
+                   "kv_heads": case.hkv, "head_dim": case.d, "kv_dtype": fmt_kv,
+                   "page": 64, "window": window, "splits": splits, "kv_pool_copies": len(pools)},
+        "hbm_gbps": achieved,
+        "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
+        "call_us_mean": call_ms * 1e3,
+        "call_us_p10_p90": [float(np.percentile(per_call_ms, 10) * 1e3),
+                            float(np.percentile(per_call_ms, 90) * 1e3)],
+        "algorithmic_bytes_per_call": nbytes,
+        "flops_per_call": flops,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "timed": "HIP events around each call on the launch stream"},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample of the same workload")
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,21 @@
+"""MFA decode attention for MI355X (gfx950): a C-ABI HIP library plus a thin
+PyTorch binding.  Importing this package does not load the library; the first
+call does, and fails loudly if it has not been built."""
+
+from .binding import (
+    decode_desc,
+    mfa_decode_attention,
+    mfa_decode_attention_gqa,
+    mfa_decode_plan_splits,
+    mfa_decode_workspace_size,
+    mfa_query_proj,
+)
+
+__all__ = [
+    "decode_desc",
+    "mfa_decode_attention",
+    "mfa_decode_attention_gqa",
+    "mfa_decode_plan_splits",
+    "mfa_decode_workspace_size",
+    "mfa_query_proj",
+]

@@ -1,0 +1,136 @@
+"""Thin PyTorch binding over the C ABI: argument marshalling only.
+
+Each function reads shapes, dtypes, data pointers and the current stream from
+torch tensors, fills the descriptor and calls the library entry point of the
+same name.  Every step of the computation runs in the HIP kernels.  A missing
+library raises (decode_attention_mfa_amd._lib.LibraryNotBuilt).
+
+Workspaces: pass `workspace=` (a uint8 CUDA tensor, 256-byte aligned) to keep
+calls allocation-free (e.g. under graph capture); otherwise a per-device
+workspace is grown on demand and reused, so calls that use the default
+workspace must be ordered on one stream.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MFA_BF16, MFA_F32, MFA_FP8_E4M3, MfaDecodeDesc, MfaQueryProjDesc, check
+
+PAGE = 64
+_workspaces = {}
+
+
+def _dtype_code(t, allow_fp8=False):
+    if t.dtype == torch.float32:
+        return MFA_F32
+    if t.dtype == torch.bfloat16:
+        return MFA_BF16
+    if allow_fp8 and t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MFA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(device, nbytes, given):
+    if nbytes == 0:
+        return given, 0 if given is None else given.numel()
+    if given is not None:
+        return given, given.numel()
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    off = (-ws.data_ptr()) % 256
+    return ws[off:], ws.numel() - off
+
+
+def decode_desc(q, k_cache, block_table, out, num_splits=0):
+    """Build an MfaDecodeDesc from tensors (paged when block_table is given)."""
+    B, hq, d = q.shape
+    if block_table is not None:
+        hkv = k_cache.shape[1]
+        max_blocks = block_table.shape[1]
+        num_blocks = k_cache.shape[0]
+    else:
+        hkv = k_cache.shape[2]
+        max_blocks = k_cache.shape[1] // PAGE
+        num_blocks = 0
+    return MfaDecodeDesc(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=PAGE,
+                         max_blocks_per_seq=max_blocks, num_blocks=num_blocks,
+                         q_dtype=_dtype_code(q), kv_dtype=_dtype_code(k_cache, allow_fp8=True),
+                         out_dtype=_dtype_code(out), num_splits=int(num_splits))
+
+
+def mfa_decode_workspace_size(desc, window=0):
+    return int(_lib.load().mfa_decode_workspace_size(ctypes.byref(desc), int(window)))
+
+
+def mfa_decode_plan_splits(desc, window=0, num_cus=256):
+    return int(_lib.load().mfa_decode_plan_splits(ctypes.byref(desc), int(window), int(num_cus)))
+
+
+def _decode(entry, q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_scale, v_scale,
+            window, num_splits, workspace, stream):
+    lib = _lib.load()
+    desc = decode_desc(q, k_cache, block_table, out, num_splits)
+    need = mfa_decode_workspace_size(desc, window)
+    ws, ws_bytes = _workspace(q.device, need, workspace)
+    args = [ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(ctx_lens), _ptr(k_scale), _ptr(v_scale), _ptr(out), ctypes.c_float(scale)]
+    if entry == "gqa":
+        args.append(ctypes.c_int32(int(window)))
+        status = lib.mfa_decode_attention_gqa(*args, _ptr(ws), ctypes.c_size_t(ws_bytes),
+                                              _stream(q, stream))
+    else:
+        status = lib.mfa_decode_attention(*args, _ptr(ws), ctypes.c_size_t(ws_bytes),
+                                          _stream(q, stream))
+    check(status)
+    return out
+
+
+def mfa_decode_attention(q, k_cache, v_cache, block_table, ctx_lens, out, scale, *,
+                         k_scale=None, v_scale=None, num_splits=0, workspace=None, stream=None):
+    """MFA (MQA, one KV head) decode attention; see mfa_decode_attention in the header."""
+    return _decode("mqa", q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_scale,
+                   v_scale, 0, num_splits, workspace, stream)
+
+
+def mfa_decode_attention_gqa(q, k_cache, v_cache, block_table, ctx_lens, out, scale, *,
+                             window=0, k_scale=None, v_scale=None, num_splits=0, workspace=None,
+                             stream=None):
+    """GQA / sliding-window decode attention; see mfa_decode_attention_gqa."""
+    return _decode("gqa", q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_scale,
+                   v_scale, window, num_splits, workspace, stream)
+
+
+def query_proj_desc(x, w_qup, q_out, num_heads, eps):
+    B, hidden = x.shape
+    rank = w_qup.shape[1]
+    width = w_qup.shape[0]
+    return MfaQueryProjDesc(batch=B, hidden=hidden, rank=rank, num_heads=num_heads,
+                            head_dim=width // num_heads, eps=float(eps),
+                            out_dtype=_dtype_code(q_out))
+
+
+def mfa_query_proj(x, w_qdown, w_qup, q_out, *, num_heads=64, gain=None, eps=1e-6,
+                   workspace=None, stream=None):
+    """Low-rank query path; weights in [out, in] layout; see mfa_query_proj."""
+    lib = _lib.load()
+    desc = query_proj_desc(x, w_qup, q_out, num_heads, eps)
+    need = int(lib.mfa_query_proj_workspace_size(ctypes.byref(desc)))
+    ws, ws_bytes = _workspace(x.device, need, workspace)
+    check(lib.mfa_query_proj(ctypes.byref(desc), _ptr(x), _ptr(w_qdown), _ptr(w_qup),
+                             _ptr(gain), _ptr(q_out), _ptr(ws), ctypes.c_size_t(ws_bytes),
+                             _stream(x, stream)))
+    return q_out

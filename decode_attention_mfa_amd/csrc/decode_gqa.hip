@@ -1,0 +1,311 @@
+// GQA / sliding-window decode attention on gfx950: 16 query heads share each
+// KV group, d = 192 or 256 ("Step-5-Preview: Sparse GQA, Indexer und
+// KV-Speicher": 64 query heads, 4 KV groups, width 192, head h reads group
+// floor(h / 16); local layers attend to a 512-token window that includes the
+// current token; the dense global layer attends to everything).
+//
+// Workgroup = 4 waves = one (slot, KV group, split).  The split's keys are
+// streamed in 64-key tiles through the same LDS phase ring as the MQA kernel
+// (phase 2t = K tile [64][d], phase 2t+1 = V^T tile [d][64], 16-byte
+// global->LDS DMA, kRing - 2 phases in flight).  With 16 heads per group a
+// single MFMA row block covers all heads, so the waves split the keys
+// instead: wave w takes keys 16w .. 16w+15 of every tile.
+//   S^T[key, head] = K . Q^T            16x16x32 bf16 MFMA, d/32 K-steps
+//   O^T[ch, head] += V^T . P^T          16x16x16 bf16 MFMA over the wave's
+//                                       16 keys (the S^T lane layout is the
+//                                       B operand as is)
+// Each wave keeps its own online softmax (m, l, O) over its key subset; the
+// four are merged through LDS at the end (the same log-sum-exp merge as the
+// split combine).
+#include "device_common.h"
+#include "kernel_params.h"
+
+namespace mfa {
+namespace {
+
+constexpr int kG = 16;
+constexpr int kMaxChunkTiles = 2048;
+constexpr float kLazyRescale = 8.f;
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+
+__device__ __forceinline__ floatx4 mfma_bf16_16x16x16(intx2 a, intx2 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                   __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+}
+
+template <int D>
+struct GqaCfg {
+  static constexpr int kPhaseBytes = 64 * D * 2;                  // one K or V^T tile
+  static constexpr int kRing = D == 192 ? 6 : 4;                   // LDS slots
+  static constexpr int kAhead = kRing - 2;                         // phases in flight while computing
+  static constexpr int kDmaPerWave = kPhaseBytes / 1024 / 4;       // 16-byte copies per lane per phase
+  static constexpr int kChunks = D / 8;                            // 16-byte chunks per K row
+};
+
+// K rows (2D bytes): XOR the chunk index with a key-dependent value so the 16
+// lanes of one MFMA operand read 16 distinct bank quads.  d = 192 keeps the
+// XOR inside aligned groups of 8 chunks (24 chunks per row).
+template <int D>
+__device__ __forceinline__ int swz_k(int key) {
+  return D == 256 ? (key & 15) : ((key & 7) ^ ((key >> 3) & 1));
+}
+// V^T rows (128 bytes, 8 chunks).
+__device__ __forceinline__ int swz_v(int ch) { return (ch & 7) ^ ((ch >> 3) & 1); }
+
+template <int N>
+__device__ __forceinline__ void phase_barrier() {
+  wait_vmcnt<N>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
+  using C = GqaCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[C::kRing * C::kPhaseBytes];
+  __shared__ int blk_ids[kMaxChunkTiles];
+  __shared__ float wave_ml[4][kG][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int q4 = lane >> 4;
+  const int bg = blockIdx.y;
+  const int b = bg / p.hkv;
+  const int g = bg - b * p.hkv;
+  const int split = blockIdx.x;
+  const int L = p.ctx_lens[b];
+  const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+  int n_tiles = 0, t_lo = 0;
+  if (L > 0) {
+    t_lo = lo / kPage;
+    n_tiles = (L - 1) / kPage - t_lo + 1;
+  }
+  const int t_begin = t_lo + split * p.chunk_tiles;
+  const int t_end = min(t_lo + n_tiles, t_begin + p.chunk_tiles);
+  const int head = g * kG + r;          // this lane's query head
+
+  if (t_begin >= t_end) {
+    if (p.splits == 1) {   // empty slot: zeros (wave w writes channel tiles w, w+4, ...)
+      for (int ct = wave; ct < D / 16; ct += 4) {
+        const int64_t o = ((int64_t)b * p.hq + head) * D + ct * 16 + q4 * 4;
+        if (p.out_f32)
+          *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
+        else
+          *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
+      }
+    }
+    return;
+  }
+  const int nt = t_end - t_begin;
+  const int nphase = 2 * nt;
+  const float qk_scale = p.scale * kLog2e * (p.k_scale ? p.k_scale[g] : 1.f);
+  const float v_scale = p.v_scale ? p.v_scale[g] : 1.f;
+
+  for (int i = threadIdx.x; i < nt; i += 256)
+    blk_ids[i] = p.block_table ? p.block_table[(int64_t)b * p.max_blocks + t_begin + i] : 0;
+
+  // Q fragments: head r of the group, channels 32s + 8q4 .. +7.
+  intx4 qf[D / 32];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * D + q4 * 8;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qf[s] = *reinterpret_cast<const intx4*>(qp + s * 32);
+  }
+  wait_vmcnt<0>();   // the copies below are invisible to the compiler's wait bookkeeping
+  __syncthreads();
+
+  const uint16_t* kpool = static_cast<const uint16_t*>(p.k);
+  const uint16_t* vpool = static_cast<const uint16_t*>(p.v);
+  auto issue_phase = [&](int ph_req, uint8_t* dst) {
+    const int ph = ph_req < nphase ? ph_req : nphase - 2 + (ph_req & 1);
+    const int tile_rel = ph >> 1;
+    const int tile = t_begin + tile_rel;
+    const uint16_t* kt;
+    const uint16_t* vt;
+    if (p.block_table) {
+      const int64_t blk = readfirstlane(blk_ids[tile_rel]);
+      kt = kpool + blk * p.k_block_stride + (int64_t)g * p.k_head_stride;
+      vt = vpool + blk * p.v_block_stride + (int64_t)g * p.v_head_stride;
+    } else {
+      kt = kpool + ((int64_t)b * p.max_blocks + tile) * p.k_block_stride + (int64_t)g * p.k_head_stride;
+      vt = vpool + (int64_t)b * p.v_seq_stride + (int64_t)g * p.v_head_stride + (int64_t)tile * kPage;
+    }
+    if ((ph & 1) == 0) {
+      // K tile: 64 rows of D/8 chunks; copy i covers 1 KB = 64 chunks.
+#pragma unroll
+      for (int k = 0; k < C::kDmaPerWave; ++k) {
+        const int i = wave * C::kDmaPerWave + k;
+        const int idx = i * 64 + lane;                 // chunk index in the tile
+        const int row = idx / C::kChunks;
+        const int ch = (idx - row * C::kChunks) ^ swz_k<D>(row);
+        dma16(kt + row * p.k_row_stride + ch * 8, dst + i * 1024);
+      }
+    } else {
+      // V^T tile: D rows of 8 chunks (64 keys); copy i covers 8 rows.
+#pragma unroll
+      for (int k = 0; k < C::kDmaPerWave; ++k) {
+        const int i = wave * C::kDmaPerWave + k;
+        const int row = 8 * i + (lane >> 3);
+        const int ch = (lane & 7) ^ swz_v(row);
+        dma16(vt + row * p.v_row_stride + ch * 8, dst + i * 1024);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int ph = 0; ph < C::kRing - 1; ++ph) issue_phase(ph, ring + ph * C::kPhaseBytes);
+
+  const int my_key = 16 * wave + r;                    // K operand row of this lane
+  const int xk = swz_k<D>(my_key);
+  const int xv = swz_v(r);
+
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  floatx4 acc[D / 16];
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+  intx2 pb;
+
+  auto k_phase = [&](const uint8_t* buf, int key0) {
+    floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const int chunk = (4 * s + q4) ^ xk;
+      const intx4 a = *reinterpret_cast<const intx4*>(buf + my_key * (2 * D) + chunk * 16);
+      st = mfma_bf16_16x16x32(a, qf[s], st);
+    }
+    float sv[4];
+    const bool partial = (key0 < lo) || (key0 + kPage > L);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = st[i] * qk_scale;
+      if (partial) {
+        const int key = key0 + 16 * wave + 4 * q4 + i;
+        x = (key >= lo && key < L) ? x : kNegInf;
+      }
+      sv[i] = x;
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = wave_max_xor16_32(mx);
+    // A wave can see a tile whose 16 keys are all masked: mx = -inf, nothing moves.
+    const bool move = mx > m_run + kLazyRescale;
+    const float m_new = move ? mx : m_run;
+    if (__any(move && m_run != kNegInf)) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) acc[ct] *= alpha;
+    }
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = (m_new == kNegInf) ? 0.f : fast_exp2(sv[i] - m_new);
+      psum += sv[i];
+    }
+    l_run += psum;
+    pb = intx2{(int)pack_bf16x2(sv[0], sv[1]), (int)pack_bf16x2(sv[2], sv[3])};
+  };
+
+  auto v_phase = [&](const uint8_t* buf, int key0) {
+    const int kfirst = 16 * wave + 4 * q4;             // this lane's 4 keys
+    const int vvalid = L - key0;
+    uint32_t keep0 = 0xffffffffu, keep1 = 0xffffffffu;
+    if (vvalid < kPage) {   // rows past the end may hold NaN
+      keep0 = ((kfirst + 0 < vvalid) ? 0x0000ffffu : 0u) | ((kfirst + 1 < vvalid) ? 0xffff0000u : 0u);
+      keep1 = ((kfirst + 2 < vvalid) ? 0x0000ffffu : 0u) | ((kfirst + 3 < vvalid) ? 0xffff0000u : 0u);
+    }
+    const int chunk = (kfirst >> 3) ^ xv;
+    const int half = (q4 & 1) * 8;
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct) {
+      intx2 a = *reinterpret_cast<const intx2*>(buf + ct * 2048 + r * 128 + chunk * 16 + half);
+      a.x &= keep0;
+      a.y &= keep1;
+      acc[ct] = mfma_bf16_16x16x16(a, pb, acc[ct]);
+    }
+  };
+
+  auto step = [&](int ph, int slot) {
+    phase_barrier<C::kAhead * C::kDmaPerWave>();
+    issue_phase(ph + C::kRing - 1, ring + ((slot + C::kRing - 1) % C::kRing) * C::kPhaseBytes);
+    const uint8_t* cur = ring + slot * C::kPhaseBytes;
+    const int key0 = (t_begin + (ph >> 1)) * kPage;
+    if ((slot & 1) == 0) k_phase(cur, key0);
+    else v_phase(cur, key0);
+  };
+
+  for (int ph = 0; ph < nphase; ph += C::kRing) {
+#pragma unroll
+    for (int s = 0; s < C::kRing; s += 2) {
+      if (ph + s >= nphase) break;
+      step(ph + s, s);
+      step(ph + s + 1, s + 1);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();   // every wave is done with the ring: reuse it for the merge
+
+  // ---- merge the four waves' (m, l, O) ----
+  const float l_w = wave_sum_xor16_32(l_run);
+  if (q4 == 0) {
+    wave_ml[wave][r][0] = m_run;
+    wave_ml[wave][r][1] = l_w;
+  }
+  float* obuf = reinterpret_cast<float*>(ring);        // [4][kG][D]
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct)
+    *reinterpret_cast<floatx4*>(obuf + ((wave * kG + r) * D + ct * 16 + q4 * 4)) = acc[ct];
+  __syncthreads();
+
+  // Thread t: head t / 16, channels 4*(t % 16) + 64*k.
+  const int h = threadIdx.x >> 4;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, wave_ml[w][h][0]);
+  float wgt[4];
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wgt[w] = (wave_ml[w][h][0] == kNegInf) ? 0.f : fast_exp2(wave_ml[w][h][0] - M);
+    lsum += wgt[w] * wave_ml[w][h][1];
+  }
+  const int64_t ghead = (int64_t)g * kG + h;
+  const int64_t prow = ((int64_t)bg * p.splits + split) * kG + h;
+  for (int c4 = (threadIdx.x & 15) * 4; c4 < D; c4 += 64) {
+    floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o += wgt[w] * *reinterpret_cast<const floatx4*>(obuf + (w * kG + h) * D + c4);
+    if (p.splits == 1) {
+      const floatx4 v = o * (v_scale / lsum);
+      const int64_t off = ((int64_t)b * p.hq + ghead) * D + c4;
+      if (p.out_f32)
+        *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + off) = v;
+      else
+        *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + off) =
+            intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
+    } else {
+      *reinterpret_cast<floatx4*>(p.part_o + prow * D + c4) = o;
+    }
+  }
+  if (p.splits > 1 && (threadIdx.x & 15) == 0)
+    *reinterpret_cast<floatx2*>(p.part_ml + prow * 2) = floatx2{M, lsum};
+}
+
+}  // namespace
+
+hipError_t launch_gqa(const DecodeParams& p, int d, hipStream_t stream) {
+  dim3 grid(p.splits, p.batch * p.hkv);
+  if (d == 192)
+    hipLaunchKernelGGL(gqa_decode_bf16_kernel<192>, grid, dim3(256), 0, stream, p);
+  else if (d == 256)
+    hipLaunchKernelGGL(gqa_decode_bf16_kernel<256>, grid, dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mfa

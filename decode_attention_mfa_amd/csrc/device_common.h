@@ -1,0 +1,88 @@
+// Device helpers for gfx950 (CDNA4): MFMA wrappers, bf16/FP8 conversion,
+// LDS-DMA loads, wave reductions.  Wave size is 64 throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) float floatx4;
+typedef __attribute__((ext_vector_type(2))) float floatx2;
+typedef __attribute__((ext_vector_type(4))) int intx4;
+typedef __attribute__((ext_vector_type(2))) int intx2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Operand layout (lane l,
+// wave64): A row = l % 16, B column = l % 16, both hold the 8 consecutive
+// K-indices 8*(l/16) .. 8*(l/16)+7.  Result: lane l holds D[4*(l/16)+i][l%16],
+// i = 0..3.
+__device__ __forceinline__ floatx4 mfma_bf16_16x16x32(intx4 a, intx4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Exact widening of four OCP E4M3FN bytes (one dword) to four bf16 (two
+// dwords).  Every E4M3 value is representable in bf16, so the hardware
+// conversion (fp8 -> fp32, then fp32 -> bf16) is exact.
+__device__ __forceinline__ intx2 e4m3x4_to_bf16x4(uint32_t w) {
+  floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  intx2 r;
+  r.x = (int)pack_bf16x2(a.x, a.y);
+  r.y = (int)pack_bf16x2(b.x, b.y);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte global -> LDS copy without a register round trip
+// (global_load_lds_dwordx4).  Lane l of the wave writes lds_base + 16*l;
+// lds_base must be wave-uniform.  Issued through inline asm on purpose: the
+// compiler's own wait insertion for LDS DMA cannot tell ring slots apart and
+// would drain every in-flight copy before each LDS read.  Callers therefore
+// own the synchronisation: wait_vmcnt<N>() for their own copies, then a
+// workgroup barrier before other waves read the slot.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ float wave_max_xor16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_xor16_32(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace mfa

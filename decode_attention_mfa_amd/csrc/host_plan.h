@@ -1,0 +1,60 @@
+// Host-side validation and launch planning for the decode entry points.
+// Plain C++ with no HIP calls, so every error path can be exercised on a
+// machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mfa_decode.h"
+
+namespace mfa {
+
+enum class DecodePath : int {
+  kMqaShared = 0,   // 64 heads per KV head, d = 256, bf16: shared-tile MFMA kernel
+  kGqaSplitKeys = 1,// 16 heads per KV head, d in {192, 256}, bf16: key-split MFMA kernel
+  kF32 = 2,         // fp32 storage: vector-ALU kernel
+};
+
+struct DecodePlan {
+  DecodePath path;
+  int32_t group;          // Hq / Hkv
+  int32_t splits;         // >= 1
+  int32_t chunk_pages;    // 64-key pages per split
+  int32_t pages_cap;      // most pages one slot can touch
+  size_t part_o_offset;   // bytes into the workspace
+  size_t part_ml_offset;
+  size_t workspace_bytes; // 0 when splits == 1
+};
+
+// Largest chunk a split may cover (block ids cached per workgroup).
+constexpr int32_t kMaxChunkPages = 2048;
+// Workspace regions are aligned to this many bytes.
+constexpr size_t kWorkspaceAlign = 256;
+
+// Validate sizes and dtypes (no pointers).  `mqa_entry` applies the MQA
+// entry's extra rule Hkv == 1.
+mfa_status validate_decode_desc(const mfa_decode_desc* d, int32_t window, bool mqa_entry);
+
+// Validate the pointer arguments of a call whose descriptor is valid.
+mfa_status validate_decode_ptrs(const mfa_decode_desc* d, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* ctx_lens,
+                                const float* k_scale, const float* v_scale, const void* out,
+                                float scale);
+
+// Path, split count and workspace layout for a valid descriptor.  num_cus is
+// only used when desc->num_splits == 0.
+DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus);
+
+mfa_status validate_query_proj_desc(const mfa_query_proj_desc* d);
+
+struct QueryProjPlan {
+  int32_t k_splits;        // split-K factor of the down projection
+  size_t y_partial_offset; // fp32 [k_splits, batch, rank]
+  size_t r_offset;         // bf16 hi/lo [2, batch, rank]
+  size_t workspace_bytes;
+};
+
+QueryProjPlan plan_query_proj(const mfa_query_proj_desc* d);
+
+}  // namespace mfa

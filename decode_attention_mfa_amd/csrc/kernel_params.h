@@ -1,0 +1,51 @@
+// Parameter blocks shared by the host launchers and the decode kernels.
+// Plain C++ (no HIP types) so the host-side planning code can include it.
+#pragma once
+
+#include <stdint.h>
+
+namespace mfa {
+
+constexpr int kPage = 64;          // tokens per cache block
+constexpr int kTile = 32;          // keys per pipeline tile (half a block)
+constexpr int kTilesPerPage = kPage / kTile;
+
+enum class KvType : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+// One decode-attention launch.  Element strides are in elements of the KV
+// storage type.  For a paged cache the K/V tile of (slot b, tile t, group g)
+// starts at   k + block * k_block_stride + g * k_head_stride + (t % 2) * 32 * k_row_stride
+//             v + block * v_block_stride + g * v_head_stride + (t % 2) * 32
+// with block = block_table[b * max_blocks + t / 2]; for a contiguous cache
+// the block index is replaced by (b * max_blocks + t / 2) for K and the V tile
+// starts at v + b * v_seq_stride + g * v_head_stride + t * 32.
+struct DecodeParams {
+  const void* q;              // [B, Hq, d]
+  const void* k;
+  const void* v;
+  const int32_t* block_table; // nullptr: contiguous
+  const int32_t* ctx_lens;    // [B]
+  const float* k_scale;       // [Hkv] (FP8) or nullptr
+  const float* v_scale;
+  void* out;                  // [B, Hq, d]
+  float* part_o;              // [B*Hkv, splits, G, d]   (splits > 1)
+  float* part_ml;             // [B*Hkv, splits, G, 2]   (splits > 1)
+  float scale;                // logit scale
+  int32_t batch;
+  int32_t hq;
+  int32_t hkv;
+  int32_t max_blocks;         // block-table row length / capacity in blocks
+  int32_t window;             // 0 = dense
+  int32_t splits;             // >= 1
+  int32_t chunk_tiles;        // 32-key tiles per split
+  int32_t out_f32;            // 1: out is fp32, else bf16
+  int64_t k_block_stride;
+  int64_t k_head_stride;
+  int64_t k_row_stride;       // elements between consecutive keys
+  int64_t v_block_stride;
+  int64_t v_head_stride;
+  int64_t v_row_stride;       // elements between consecutive channels
+  int64_t v_seq_stride;       // contiguous V: elements between slots
+};
+
+}  // namespace mfa

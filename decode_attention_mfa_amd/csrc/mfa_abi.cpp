@@ -1,0 +1,212 @@
+// C-ABI entry points of the MFA decode library (see include/mfa_decode.h).
+// Each call validates on the host, then only enqueues kernels on the caller's
+// stream: no allocation, no synchronisation, no device reads on the host.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "host_plan.h"
+#include "kernel_params.h"
+
+namespace mfa {
+hipError_t launch_mqa_bf16(const DecodeParams& p, bool split_p, hipStream_t stream);
+hipError_t launch_gqa(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_f32(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream);
+mfa_status query_proj_enqueue(const mfa_query_proj_desc* d, const QueryProjPlan& pl,
+                              const void* x, const void* w_down, const void* w_up,
+                              const float* gain, void* q_out, void* workspace,
+                              hipStream_t stream);
+}  // namespace mfa
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device, cached per device (-1 on error).
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& pl, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens,
+                              const float* k_scale, const float* v_scale, void* out, float scale,
+                              int32_t window, void* workspace) {
+  using mfa::kPage;
+  mfa::DecodeParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.k_scale = d->kv_dtype == MFA_FP8_E4M3 ? k_scale : nullptr;
+  p.v_scale = d->kv_dtype == MFA_FP8_E4M3 ? v_scale : nullptr;
+  p.out = out;
+  if (pl.splits > 1) {
+    p.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_offset);
+    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_ml_offset);
+  }
+  p.scale = scale;
+  p.batch = d->batch;
+  p.hq = d->num_q_heads;
+  p.hkv = d->num_kv_heads;
+  p.max_blocks = d->max_blocks_per_seq;
+  p.window = window;
+  p.splits = pl.splits;
+  p.chunk_tiles = pl.chunk_pages;
+  p.out_f32 = d->out_dtype == MFA_F32;
+  const int64_t hd = d->head_dim, hkv = d->num_kv_heads;
+  if (block_table) {
+    p.k_block_stride = hkv * kPage * hd;
+    p.k_head_stride = kPage * hd;
+    p.k_row_stride = hd;
+    p.v_block_stride = hkv * hd * kPage;
+    p.v_head_stride = hd * kPage;
+    p.v_row_stride = kPage;
+    p.v_seq_stride = 0;
+  } else {
+    const int64_t cap = (int64_t)d->max_blocks_per_seq * kPage;
+    p.k_block_stride = kPage * hkv * hd;
+    p.k_head_stride = hd;
+    p.k_row_stride = hkv * hd;
+    p.v_block_stride = 0;
+    p.v_head_stride = hd * cap;
+    p.v_row_stride = cap;
+    p.v_seq_stride = hkv * hd * cap;
+  }
+  return p;
+}
+
+mfa_status decode_impl(const mfa_decode_desc* d, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
+                       const float* k_scale, const float* v_scale, void* out, float scale,
+                       int32_t window, void* workspace, size_t workspace_bytes,
+                       mfa_stream_t stream, bool mqa_entry) {
+  mfa_status st = mfa::validate_decode_desc(d, window, mqa_entry);
+  if (st != MFA_OK) return st;
+  if (d->batch == 0) return MFA_OK;
+  st = mfa::validate_decode_ptrs(d, q, k_cache, v_cache, ctx_lens, k_scale, v_scale, out, scale);
+  if (st != MFA_OK) return st;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) % mfa::kWorkspaceAlign))
+    return MFA_ERR_ALIGN;
+  int cus = 0;
+  if (d->num_splits == 0) {
+    cus = device_cu_count();
+    if (cus <= 0) return MFA_ERR_LAUNCH;
+  }
+  const mfa::DecodePlan pl = mfa::plan_decode(d, window, cus);
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
+    return MFA_ERR_WORKSPACE;
+
+  const mfa::DecodeParams p = make_params(d, pl, q, k_cache, v_cache, block_table, ctx_lens,
+                                          k_scale, v_scale, out, scale, window, workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  switch (pl.path) {
+    case mfa::DecodePath::kMqaShared:
+      e = mfa::launch_mqa_bf16(p, /*split_p=*/false, s);
+      break;
+    case mfa::DecodePath::kGqaSplitKeys:
+      e = mfa::launch_gqa(p, d->head_dim, s);
+      break;
+    case mfa::DecodePath::kF32:
+      e = mfa::launch_f32(p, d->head_dim, s);
+      break;
+  }
+  if (e != hipSuccess) return MFA_ERR_LAUNCH;
+  if (pl.splits > 1 && pl.path != mfa::DecodePath::kF32) {
+    e = mfa::launch_combine(p, pl.group, d->head_dim, s);
+    if (e != hipSuccess) return MFA_ERR_LAUNCH;
+  }
+  return MFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mfa_status mfa_decode_attention(const mfa_decode_desc* desc, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table,
+                                const int32_t* ctx_lens, const float* k_scale,
+                                const float* v_scale, void* out, float scale, void* workspace,
+                                size_t workspace_bytes, mfa_stream_t stream) {
+  return decode_impl(desc, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
+                     scale, 0, workspace, workspace_bytes, stream, /*mqa_entry=*/true);
+}
+
+mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    const float* k_scale, const float* v_scale, void* out,
+                                    float scale, int32_t window, void* workspace,
+                                    size_t workspace_bytes, mfa_stream_t stream) {
+  return decode_impl(desc, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
+                     scale, window, workspace, workspace_bytes, stream, /*mqa_entry=*/false);
+}
+
+size_t mfa_decode_workspace_size(const mfa_decode_desc* desc, int32_t window) {
+  if (mfa::validate_decode_desc(desc, window, false) != MFA_OK) return 0;
+  int cus = 0;
+  if (desc->num_splits == 0) {
+    cus = device_cu_count();
+    if (cus <= 0) return 0;
+  }
+  return mfa::plan_decode(desc, window, cus).workspace_bytes;
+}
+
+int32_t mfa_decode_plan_splits(const mfa_decode_desc* desc, int32_t window, int32_t num_cus) {
+  if (mfa::validate_decode_desc(desc, window, false) != MFA_OK) return 0;
+  return mfa::plan_decode(desc, window, num_cus > 0 ? num_cus : 1).splits;
+}
+
+mfa_status mfa_query_proj(const mfa_query_proj_desc* desc, const void* x, const void* w_qdown,
+                          const void* w_qup, const float* gain, void* q_out, void* workspace,
+                          size_t workspace_bytes, mfa_stream_t stream) {
+  mfa_status st = mfa::validate_query_proj_desc(desc);
+  if (st != MFA_OK) return st;
+  if (desc->batch == 0) return MFA_OK;
+  if (!x || !w_qdown || !w_qup || !q_out) return MFA_ERR_NULL;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_qdown) |
+                        reinterpret_cast<uintptr_t>(w_qup) | reinterpret_cast<uintptr_t>(q_out);
+  if (mis & 15u) return MFA_ERR_ALIGN;
+  const mfa::QueryProjPlan pl = mfa::plan_query_proj(desc);
+  if (!workspace || workspace_bytes < pl.workspace_bytes) return MFA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % mfa::kWorkspaceAlign) return MFA_ERR_ALIGN;
+  return mfa::query_proj_enqueue(desc, pl, x, w_qdown, w_qup, gain, q_out, workspace,
+                                 reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t mfa_query_proj_workspace_size(const mfa_query_proj_desc* desc) {
+  if (mfa::validate_query_proj_desc(desc) != MFA_OK) return 0;
+  return mfa::plan_query_proj(desc).workspace_bytes;
+}
+
+const char* mfa_status_string(mfa_status s) {
+  switch (s) {
+    case MFA_OK: return "ok";
+    case MFA_ERR_NULL: return "a required pointer is NULL";
+    case MFA_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MFA_ERR_SHAPE: return "sizes inconsistent or outside the supported set";
+    case MFA_ERR_ALIGN: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case MFA_ERR_ARG: return "invalid argument (negative window or non-finite scale)";
+    case MFA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MFA_ERR_LAUNCH: return "HIP runtime refused a launch";
+  }
+  return "unknown status";
+}
+
+int32_t mfa_abi_version(void) { return MFA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+/*
+ * mfa_decode.h -- C ABI of the MI355X (gfx950) MFA decode-attention library.
+ *
+ * What the library computes
+ *   One decode step of Multi-matrix Factorization Attention (MFA): every slot
+ *   of the batch contributes one new query token with Hq = 64 heads of width
+ *   d = 256, and all heads attend to ONE shared K head and ONE shared V head
+ *   over the slot's whole cache ("Step-3 is Large yet Affordable",
+ *   section 2 "Step-3 model card", Table 1).  For head h and slot b with
+ *   L = ctx_lens[b] keys:
+ *       s_j   = scale * <q[b,h,:], K_j>             j in [lo, L)
+ *       out   = sum_j softmax(s)_j * V_j
+ *   with lo = 0 (dense) or max(0, L - window) for a sliding window that counts
+ *   the current token ("Step-5-Preview: Sparse GQA, Indexer und
+ *   KV-Speicher", backbone table and the attention equation of section
+ *   "Die eigentliche Attention liest weiterhin originale K/V", which also
+ *   gives the GQA head-to-group map g(h) = floor(h / (Hq/Hkv))).
+ *   L counts the token appended in this step (duck-llm chapter 7, section
+ *   7.6: the decode kernel must see cached_len + 1).
+ *
+ * Cache layouts (P = page_size = 64 tokens per block; d contiguous for K,
+ * tokens contiguous for V -- V blocks are channel-major so that a 16-byte
+ * load gives 8 consecutive keys of one channel, the operand shape of the
+ * PV matrix product):
+ *   paged       K: [num_blocks, Hkv, P, d]      V: [num_blocks, Hkv, d, P]
+ *               logical position j of slot b is row j % P of block
+ *               block_table[b * max_blocks_per_seq + j / P]
+ *   contiguous  (block_table == NULL)
+ *               K: [B, cap, Hkv, d]             V: [B, Hkv, d, cap]
+ *               with cap = max_blocks_per_seq * P
+ *   Rows at positions >= L inside a slot's last block may hold anything,
+ *   NaN included: they are never used.  Block-table entries past the last
+ *   block a slot uses are never read (callers pad with -1).
+ *
+ * Ownership, streams, graphs
+ *   The caller owns every buffer (device memory for all data pointers).  The
+ *   library allocates nothing during a call, keeps no pointer after it
+ *   returns, reads no device data on the host and never synchronises: a call
+ *   only validates its arguments on the host and enqueues kernels on
+ *   `stream` (NULL = the null stream).  ctx_lens and the block table are read
+ *   by the kernels when they execute, so a captured graph replays correctly
+ *   after the caller updates them in place (the graph-state hazards of
+ *   duck-llm chapter 7, section 7.5).
+ *
+ * Errors
+ *   Problems detectable on the host return a non-zero mfa_status and enqueue
+ *   nothing.  Device-side contract violations (a block id outside the pool,
+ *   L > max_blocks_per_seq * P, L < 0) are undefined behaviour.
+ */
+#ifndef MFA_DECODE_H
+#define MFA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MFA_ABI_VERSION 1
+
+/* A hipStream_t (struct ihipStream_t*).  NULL means the null stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* mfa_stream_t;
+
+typedef enum mfa_status {
+  MFA_OK = 0,
+  MFA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  MFA_ERR_DTYPE = 2,       /* unsupported dtype or dtype combination             */
+  MFA_ERR_SHAPE = 3,       /* sizes inconsistent or outside the supported set    */
+  MFA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned              */
+  MFA_ERR_ARG = 5,         /* other invalid argument (negative window, bad scale)*/
+  MFA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required         */
+  MFA_ERR_LAUNCH = 7       /* the HIP runtime refused a launch                   */
+} mfa_status;
+
+typedef enum mfa_dtype {
+  MFA_F32 = 0,             /* IEEE binary32                                      */
+  MFA_BF16 = 1,            /* bfloat16                                           */
+  MFA_FP8_E4M3 = 2         /* OCP FP8 E4M3FN (bias 7, max 448, 0x7F/0xFF NaN)    */
+} mfa_dtype;
+
+/*
+ * Shape and type of one decode-attention call.
+ *   batch               B >= 0 slots (B == 0 enqueues nothing)
+ *   num_q_heads         Hq
+ *   num_kv_heads        Hkv, Hq % Hkv == 0
+ *   head_dim            d
+ *   page_size           tokens per cache block; must be 64
+ *   max_blocks_per_seq  paged: length (= row stride) of each block-table row;
+ *                       contiguous: cache capacity / 64
+ *   num_blocks          paged: blocks in each pool (documentation / checks
+ *                       only); contiguous: ignored
+ *   q_dtype, kv_dtype, out_dtype
+ *                       supported: kv BF16 or FP8_E4M3 with q BF16 and out
+ *                       BF16 or F32; kv F32 with q F32 and out F32
+ *   num_splits          0 = choose with the library's heuristic
+ *                       (mfa_decode_plan_splits); > 0 forces that many splits
+ *                       of each slot's key range
+ * Supported (Hq/Hkv, d): (64, 256) on the shared-tile MFMA path (MQA);
+ * (16, 192), (16, 256) on the per-group MFMA path (GQA); any Hq/Hkv and any
+ * d <= 256 that is a multiple of 4 with F32 storage.
+ */
+typedef struct mfa_decode_desc {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int32_t q_dtype;
+  int32_t kv_dtype;
+  int32_t out_dtype;
+  int32_t num_splits;
+} mfa_decode_desc;
+
+/*
+ * MFA decode attention (the MQA case, Hkv == 1, dense).
+ *   q            [B, Hq, d]            q_dtype, contiguous
+ *   k_cache      K pool / static cache (layouts above), kv_dtype
+ *   v_cache      V pool / static cache (layouts above), kv_dtype
+ *   block_table  [B, max_blocks_per_seq] int32 physical block ids, or NULL
+ *                for a contiguous cache
+ *   ctx_lens     [B] int32, keys per slot including the current token
+ *   k_scale      FP8 only: [Hkv] fp32 per-KV-head dequantisation scales
+ *   v_scale      (stored value = code * scale); NULL otherwise
+ *   out          [B, Hq, d]            out_dtype, written in full
+ *                (a slot with L == 0 gets zeros)
+ *   scale        logit scale, finite (1/sqrt(d) for both pages' models)
+ *   workspace    device scratch of at least mfa_decode_workspace_size(desc,0)
+ *                bytes, 256-byte aligned; may be NULL when that size is 0.
+ *                Calls that share a workspace must be ordered on one stream.
+ * All data pointers must be 16-byte aligned.
+ * Returns MFA_ERR_SHAPE when num_kv_heads != 1.
+ */
+mfa_status mfa_decode_attention(const mfa_decode_desc* desc, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* ctx_lens,
+                                const float* k_scale, const float* v_scale, void* out,
+                                float scale, void* workspace, size_t workspace_bytes,
+                                mfa_stream_t stream);
+
+/*
+ * GQA / sliding-window variant: as mfa_decode_attention, for any supported
+ * Hkv (head h reads KV group floor(h / (Hq/Hkv))) and window >= 0
+ * (0 = dense; W > 0 attends to keys [max(0, L - W), L - 1]).
+ */
+mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    const float* k_scale, const float* v_scale, void* out,
+                                    float scale, int32_t window, void* workspace,
+                                    size_t workspace_bytes, mfa_stream_t stream);
+
+/* Workspace bytes a call with this descriptor and window needs (0 when every
+ * slot fits one split).  Pure host arithmetic: no HIP call is made when
+ * desc->num_splits > 0; otherwise the current device's compute-unit count is
+ * queried once and cached. */
+size_t mfa_decode_workspace_size(const mfa_decode_desc* desc, int32_t window);
+
+/* The split heuristic (host integers only): how many chunks each slot's key
+ * range is cut into, given the device's compute-unit count.  Keeps
+ * B * Hkv * splits at or above one wave of workgroups on `num_cus` compute
+ * units while keeping chunks at least 256 keys long.  Returns >= 1, or 0 if
+ * desc is NULL or invalid. */
+int32_t mfa_decode_plan_splits(const mfa_decode_desc* desc, int32_t window, int32_t num_cus);
+
+/*
+ * Low-rank MFA query path ("Step-3 is Large yet Affordable", section 2):
+ *     y = x W_qdown^T;  r = y / sqrt(mean(y^2) + eps) * gain;  q = r W_qup^T
+ * and q is viewed as [B, num_heads, head_dim] (head h = output columns
+ * h*head_dim .. h*head_dim + head_dim - 1).
+ *   x        [batch, hidden]                      bf16, row-major
+ *   w_qdown  [rank, hidden]                       bf16, row-major ("out, in")
+ *   w_qup    [num_heads * head_dim, rank]         bf16, row-major ("out, in")
+ *   gain     [rank] fp32, or NULL for unit gain
+ *   q_out    [batch, num_heads * head_dim]        out_dtype (BF16 or F32)
+ *   workspace >= mfa_query_proj_workspace_size(desc) bytes, 256-byte aligned
+ * Supported: hidden % 64 == 0, rank % 64 == 0, rank <= 4096,
+ * (num_heads * head_dim) % 64 == 0.
+ */
+typedef struct mfa_query_proj_desc {
+  int32_t batch;
+  int32_t hidden;
+  int32_t rank;
+  int32_t num_heads;
+  int32_t head_dim;
+  float eps;
+  int32_t out_dtype;
+} mfa_query_proj_desc;
+
+mfa_status mfa_query_proj(const mfa_query_proj_desc* desc, const void* x, const void* w_qdown,
+                          const void* w_qup, const float* gain, void* q_out, void* workspace,
+                          size_t workspace_bytes, mfa_stream_t stream);
+
+size_t mfa_query_proj_workspace_size(const mfa_query_proj_desc* desc);
+
+/* Static, never-NULL description of a status code. */
+const char* mfa_status_string(mfa_status status);
+
+/* MFA_ABI_VERSION of the built library. */
+int32_t mfa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFA_DECODE_H */

@@ -1,0 +1,142 @@
+"""CPU-only tests of the C-ABI library: it loads, exports every symbol the header
+declares, and its host-side validation / planning behaves as documented.  No
+call here reaches a kernel launch (every call either fails validation first or
+is a pure planning query)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_mfa_amd import _lib
+from decode_attention_mfa_amd._lib import MFA_BF16, MFA_F32, MFA_FP8_E4M3, MfaDecodeDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="library not built (run __graft_entry__.build())")
+
+MFA_ERR_NULL, MFA_ERR_DTYPE, MFA_ERR_SHAPE, MFA_ERR_ALIGN = 1, 2, 3, 4
+MFA_ERR_ARG, MFA_ERR_WORKSPACE = 5, 6
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "mfa_decode.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(mfa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_what_binding_lists():
+    assert header_symbols() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in header_symbols():
+        assert hasattr(lib, name), name
+    assert lib.mfa_abi_version() == 1
+    for s in range(8):
+        assert lib.mfa_status_string(s)
+
+
+def desc(**kw):
+    d = dict(batch=64, num_q_heads=64, num_kv_heads=1, head_dim=256, page_size=64,
+             max_blocks_per_seq=64, num_blocks=4096, q_dtype=MFA_BF16, kv_dtype=MFA_BF16,
+             out_dtype=MFA_BF16, num_splits=4)
+    d.update(kw)
+    return MfaDecodeDesc(**d)
+
+
+# 16-byte aligned fake addresses: validation never dereferences them.
+A = ctypes.c_void_p(0x10000)
+
+
+def call_mqa(d, q=A, k=A, v=A, table=A, lens=A, ks=None, vs=None, out=A, scale=0.0625,
+             ws=None, ws_bytes=0):
+    lib = _lib.load()
+    return lib.mfa_decode_attention(ctypes.byref(d) if d is not None else None, q, k, v, table,
+                                    lens, ks, vs, out, ctypes.c_float(scale), ws,
+                                    ctypes.c_size_t(ws_bytes), None)
+
+
+def call_gqa(d, window, **kw):
+    lib = _lib.load()
+    return lib.mfa_decode_attention_gqa(ctypes.byref(d), A, A, A, A, A, None, None, A,
+                                        ctypes.c_float(0.07), ctypes.c_int32(window), None,
+                                        ctypes.c_size_t(0), None)
+
+
+def test_null_descriptor_and_pointers():
+    assert call_mqa(None) == MFA_ERR_NULL
+    assert call_mqa(desc(), q=None) == MFA_ERR_NULL
+    assert call_mqa(desc(), out=None) == MFA_ERR_NULL
+    assert call_mqa(desc(), lens=None) == MFA_ERR_NULL
+    # FP8 storage has no kernel yet: refused as a dtype before pointers are looked at
+    assert call_mqa(desc(kv_dtype=MFA_FP8_E4M3), ks=A, vs=None) == MFA_ERR_DTYPE
+
+
+def test_dtype_combinations():
+    assert call_mqa(desc(q_dtype=MFA_F32)) == MFA_ERR_DTYPE            # bf16 kv needs bf16 q
+    assert call_mqa(desc(out_dtype=MFA_FP8_E4M3)) == MFA_ERR_DTYPE
+    assert call_mqa(desc(kv_dtype=MFA_F32)) == MFA_ERR_DTYPE           # f32 kv needs f32 q/out
+    assert call_mqa(desc(kv_dtype=7)) == MFA_ERR_DTYPE
+
+
+def test_shape_rules():
+    assert call_mqa(desc(num_kv_heads=2, num_q_heads=128)) == MFA_ERR_SHAPE   # MQA entry: Hkv == 1
+    assert call_mqa(desc(page_size=32)) == MFA_ERR_SHAPE
+    assert call_mqa(desc(head_dim=128)) == MFA_ERR_SHAPE                      # not (64, 256)
+    assert call_mqa(desc(max_blocks_per_seq=0)) == MFA_ERR_SHAPE
+    assert call_mqa(desc(batch=-1)) == MFA_ERR_SHAPE
+    assert call_mqa(desc(num_splits=-2)) == MFA_ERR_SHAPE
+    assert call_gqa(desc(num_q_heads=64, num_kv_heads=3), 0) == MFA_ERR_SHAPE  # 64 % 3
+
+
+def test_alignment_scale_window_workspace():
+    assert call_mqa(desc(), q=ctypes.c_void_p(0x10008)) == MFA_ERR_ALIGN
+    assert call_mqa(desc(), out=ctypes.c_void_p(0x10004)) == MFA_ERR_ALIGN
+    assert call_mqa(desc(), scale=float("nan")) == MFA_ERR_ARG
+    assert call_mqa(desc(), scale=float("inf")) == MFA_ERR_ARG
+    assert call_gqa(desc(num_kv_heads=4, head_dim=192, num_splits=2), -1) == MFA_ERR_ARG
+    # 4 forced splits need a workspace
+    assert call_mqa(desc()) == MFA_ERR_WORKSPACE
+    assert call_mqa(desc(), ws=A, ws_bytes=16) == MFA_ERR_WORKSPACE
+    assert call_mqa(desc(), ws=ctypes.c_void_p(0x10010), ws_bytes=1 << 30) == MFA_ERR_ALIGN
+
+
+def test_empty_batch_is_a_no_op():
+    assert call_mqa(desc(batch=0), q=None, out=None) == 0
+
+
+def test_workspace_size_matches_partials():
+    lib = _lib.load()
+    d = desc(num_splits=4)
+    rows = 64 * 1 * 4 * 64
+    expect_o = rows * 256 * 4
+    got = lib.mfa_decode_workspace_size(ctypes.byref(d), 0)
+    assert got >= expect_o + rows * 8 and got % 256 == 0
+    assert lib.mfa_decode_workspace_size(ctypes.byref(desc(num_splits=1)), 0) == 0
+
+
+@pytest.mark.parametrize("batch,blocks,cus,window,expect", [
+    (64, 64, 256, 0, 4),       # B=64 x 4K: one workgroup per compute unit
+    (256, 64, 256, 0, 1),      # B=256 x 4K: no split needed
+    (1, 64, 256, 0, 16),       # one slot: 16 chunks of 4 pages
+    (2, 2, 256, 0, 1),         # tiny context: chunks never below 4 pages
+    (32, 512, 256, 512, 2),    # 512-key window touches <= 9 pages; 128 units -> 2 chunks
+])
+def test_split_heuristic(batch, blocks, cus, window, expect):
+    lib = _lib.load()
+    kv = 1 if window == 0 else 4
+    dim = 256 if window == 0 else 192
+    d = desc(batch=batch, max_blocks_per_seq=blocks, num_splits=0, num_kv_heads=kv,
+             head_dim=dim)
+    got = lib.mfa_decode_plan_splits(ctypes.byref(d), window, cus)
+    assert got == expect
+
+
+def test_forced_splits_are_honoured_up_to_the_page_count():
+    lib = _lib.load()
+    for forced, expect in [(1, 1), (3, 3), (8, 8), (100, 64)]:
+        d = desc(num_splits=forced)
+        assert lib.mfa_decode_plan_splits(ctypes.byref(d), 0, 256) == expect

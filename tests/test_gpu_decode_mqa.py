@@ -1,0 +1,139 @@
+"""GPU parity tests of MFA (MQA) decode attention against the fp64 oracle.
+
+All calls go through the C ABI (binding -> libmfa_decode.so).  Sizes are ones
+the oracle finishes in seconds while spanning several 64-key tiles, ragged
+tails (NaN-filled past each length), empty slots and every split count; the
+full-size configurations are checked on sampled slots.  Bit-exact checks:
+block permutation, single key, one-hot logits, repeat runs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode_attention
+from workloads import bf16_round_bits, config_case, make_decode_case
+
+from gpu_helpers import assert_parity, run_decode, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle(case, slots=None, **over):
+    kw = case.oracle_kwargs()
+    kw.update(over)
+    return decode_attention(case.q, case.k_cache, case.v_cache, kw.pop("ctx_lens", case.ctx_lens),
+                            case.scale, slots=slots, **kw)
+
+
+def test_config1_fp32_contiguous():
+    case = config_case(1)
+    t = to_device(case)
+    got = run_decode(case, t)
+    assert_parity(got, oracle(case), "f32", "config 1")
+
+
+RAGGED = [1, 63, 64, 65, 130, 1000, 0, 4096, 4033]
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7])
+def test_mqa_bf16_paged_ragged(splits):
+    case = make_decode_case(101, batch=len(RAGGED), ctx_lens=RAGGED, hq=64, hkv=1, d=256,
+                            scale=1 / 16)
+    t = to_device(case)
+    got = run_decode(case, t, num_splits=splits)
+    assert_parity(got, oracle(case), "bf16", f"ragged, splits={splits}")
+    assert torch.all(got[6] == 0)          # empty slot
+
+
+def test_mqa_bf16_contiguous_cache():
+    case = make_decode_case(102, batch=3, ctx_lens=[200, 64, 1], hq=64, hkv=1, d=256,
+                            paged=False, scale=1 / 16)
+    t = to_device(case)
+    got = run_decode(case, t)
+    assert_parity(got, oracle(case), "bf16", "contiguous")
+
+
+def test_mqa_fp32_output():
+    case = make_decode_case(103, batch=4, ctx_lens=[300, 5, 64, 2000], hq=64, hkv=1, d=256)
+    t = to_device(case, out_format="f32")
+    got = run_decode(case, t)
+    assert got.dtype == torch.float32
+    assert_parity(got, oracle(case), "bf16", "fp32 out")
+
+
+def test_config2_full_size_sampled_slots():
+    case = config_case(2)
+    t = to_device(case)
+    got = run_decode(case, t)
+    slots = [0, 17, 42, 63]
+    assert_parity(got[slots], oracle(case, slots=slots), "bf16", "config 2 sampled")
+    assert torch.isfinite(got.float()).all()
+
+
+def test_config3_ragged_full_size_sampled_slots():
+    case = config_case(3)
+    t = to_device(case)
+    got = run_decode(case, t)
+    order = np.argsort(case.ctx_lens)
+    slots = [int(order[0]), int(order[len(order) // 2]), int(order[-1]), 5]
+    assert_parity(got[slots], oracle(case, slots=slots), "bf16", "config 3 sampled")
+    assert torch.isfinite(got.float()).all()
+
+
+def test_block_permutation_is_bit_exact():
+    kw = dict(batch=3, ctx_lens=[777, 64, 2049], hq=64, hkv=1, d=256)
+    a = make_decode_case(104, shuffle=False, **kw)
+    b = make_decode_case(104, shuffle=True, **kw)
+    assert not np.array_equal(a.block_table, b.block_table)
+    for splits in (0, 1, 3):
+        ga = run_decode(a, to_device(a), num_splits=splits).clone()
+        gb = run_decode(b, to_device(b), num_splits=splits).clone()
+        assert torch.equal(ga.view(torch.int16), gb.view(torch.int16)), f"splits={splits}"
+
+
+def test_repeat_runs_are_bit_identical():
+    case = make_decode_case(105, batch=8, ctx_lens=[4096, 1, 300, 2500, 64, 65, 999, 3000],
+                            hq=64, hkv=1, d=256)
+    t = to_device(case)
+    first = run_decode(case, t).clone()
+    for _ in range(3):
+        again = run_decode(case, t)
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def _logical_v(case, b, j):
+    blk = case.block_table[b, j // 64]
+    return case.v_cache[blk, 0, :, j % 64]
+
+
+def test_single_key_returns_v0_exactly():
+    case = make_decode_case(106, batch=3, ctx_lens=[1, 1, 1], hq=64, hkv=1, d=256)
+    got = run_decode(case, to_device(case))
+    for b in range(3):
+        expect = torch.from_numpy(_logical_v(case, b, 0).view(np.int16))
+        assert torch.equal(got[b].view(torch.int16).cpu(), expect[None, :].expand(64, -1))
+
+
+@pytest.mark.parametrize("jstar", [0, 63, 64, 127, 1500, 2999])
+def test_one_hot_logits_select_that_value_row_exactly(jstar):
+    L = 3000
+    case = make_decode_case(107, batch=1, ctx_lens=[L], hq=64, hkv=1, d=256, scale=1 / 16)
+    q = np.zeros((1, 64, 256), np.float32)
+    q[0, :, 0] = 1.0
+    case.q = bf16_round_bits(q)
+    blk = case.block_table[0, jstar // 64]
+    case.k_cache[blk, 0, jstar % 64, 0] = bf16_round_bits(np.array([2048.0], np.float32))[0]
+    for splits in (0, 1, 5):
+        got = run_decode(case, to_device(case), num_splits=splits)
+        expect = torch.from_numpy(_logical_v(case, 0, jstar).view(np.int16))
+        assert torch.equal(got[0].view(torch.int16).cpu(), expect[None, :].expand(64, -1)), splits
+
+
+def test_length_counts_the_current_token():
+    case = make_decode_case(108, batch=1, ctx_lens=[1000], hq=64, hkv=1, d=256)
+    t = to_device(case)
+    full = run_decode(case, t).clone()
+    shorter = run_decode(case, t, lens=torch.tensor([999], dtype=torch.int32, device="cuda"))
+    assert not torch.equal(full, shorter)
+    assert_parity(shorter, oracle(case, ctx_lens=np.array([999])), "bf16", "L-1")

@@ -1,0 +1,87 @@
+"""GPU parity of the low-rank query path (mfa_query_proj) against the fp64 oracle.
+
+Weights are drawn [in, out] by the generator (the oracle's layout) and handed
+to the library transposed to its [out, in] layout."""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_mfa_amd as mfa
+from oracle import query_proj
+from workloads import config_query_inputs, make_query_inputs
+
+from gpu_helpers import TOL, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+# fp32 output: bf16 inputs are exact, the products accumulate in fp32 and the
+# normalised bottleneck is carried as a bf16 hi/lo pair (~16 mantissa bits).
+TOL_F32 = (1e-3, 1e-4)
+
+
+def _bf16(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _run(qi, out_dtype, gain=None):
+    dev = "cuda"
+    x = _bf16(qi.x, dev)
+    wd = _bf16(qi.w_down.T, dev)
+    wu = _bf16(qi.w_up.T, dev)
+    B = qi.x.shape[0]
+    out = torch.full((B, qi.num_heads * qi.head_dim), float("nan"), dtype=out_dtype, device=dev)
+    g = torch.from_numpy(gain).to(dev) if gain is not None else None
+    mfa.mfa_query_proj(x, wd, wu, out, num_heads=qi.num_heads, gain=g, eps=qi.eps)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(qi, out, gain, rows, fmt):
+    rows = np.arange(qi.x.shape[0]) if rows is None else np.asarray(rows)
+    ref = query_proj(qi.x[rows], qi.w_down, qi.w_up, fmt="bf16", eps=qi.eps, gain=gain,
+                     num_heads=qi.num_heads, head_dim=qi.head_dim)
+    got = out[torch.as_tensor(rows, device=out.device)]
+    got = got.view(len(rows), qi.num_heads, qi.head_dim)
+    if fmt == "f32":
+        g = got.float().cpu().numpy().astype(np.float64)
+        err = np.abs(g - ref)
+        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+        assert np.all(np.isfinite(g))
+        assert err.max() <= TOL_F32[0] and rel <= TOL_F32[1], (err.max(), rel)
+    else:
+        assert_parity(got, ref, "bf16", "query_proj")
+
+
+@pytest.mark.parametrize("batch", [1, 5, 64, 70])
+@pytest.mark.parametrize("out_fmt", ["bf16", "f32"])
+def test_small_shapes(batch, out_fmt):
+    rng = np.random.default_rng(1000 + batch)
+    qi = make_query_inputs(rng, batch=batch, hidden=512, rank=256, num_heads=4, head_dim=64)
+    gain = (1.0 + 0.25 * rng.standard_normal(256)).astype(np.float32)
+    out = _run(qi, torch.float32 if out_fmt == "f32" else torch.bfloat16, gain)
+    _check(qi, out, gain, None, out_fmt)
+
+
+def test_unit_gain_when_null():
+    rng = np.random.default_rng(77)
+    qi = make_query_inputs(rng, batch=9, hidden=1024, rank=128, num_heads=2, head_dim=128)
+    out = _run(qi, torch.float32, None)
+    _check(qi, out, None, None, "f32")
+
+
+def test_full_shape_sampled_rows():
+    """Step-3 query shape (hidden 7168, rank 2048, 64 x 256) at batch 256;
+    the oracle evaluates a sample of rows (rows are independent)."""
+    qi = config_query_inputs(4, batch=256)
+    out = _run(qi, torch.bfloat16)
+    rows = [0, 1, 63, 64, 127, 128, 200, 255]
+    _check(qi, out, None, rows, "bf16")
+
+
+def test_repeat_bit_identical():
+    rng = np.random.default_rng(5)
+    qi = make_query_inputs(rng, batch=33, hidden=1024, rank=512, num_heads=8, head_dim=128)
+    a = _run(qi, torch.bfloat16).clone()
+    b = _run(qi, torch.bfloat16)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
