@@ -41,15 +41,16 @@ def _stream(t, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(device, nbytes, given):
+def _workspace(device, nbytes, given, kind):
+    """A cached per-device workspace of at least nbytes, one per kind."""
     if nbytes == 0:
         return given, 0 if given is None else given.numel()
     if given is not None:
         return given, given.numel()
-    key = device.index if device.index is not None else torch.cuda.current_device()
+    key = (device.index if device.index is not None else torch.cuda.current_device(), kind)
     ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    if ws is None or ws.numel() < nbytes + 256:
+        ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     off = (-ws.data_ptr()) % 256
     return ws[off:], ws.numel() - off
@@ -85,7 +86,7 @@ def _decode(entry, q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_sca
     lib = _lib.load()
     desc = decode_desc(q, k_cache, block_table, out, num_splits)
     need = mfa_decode_workspace_size(desc, window)
-    ws, ws_bytes = _workspace(q.device, need, workspace)
+    ws, ws_bytes = _workspace(q.device, need, workspace, "decode")
     args = [ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
             _ptr(ctx_lens), _ptr(k_scale), _ptr(v_scale), _ptr(out), ctypes.c_float(scale)]
     if entry == "gqa":
@@ -129,7 +130,7 @@ def mfa_query_proj(x, w_qdown, w_qup, q_out, *, num_heads=64, gain=None, eps=1e-
     lib = _lib.load()
     desc = query_proj_desc(x, w_qup, q_out, num_heads, eps)
     need = int(lib.mfa_query_proj_workspace_size(ctypes.byref(desc)))
-    ws, ws_bytes = _workspace(x.device, need, workspace)
+    ws, ws_bytes = _workspace(x.device, need, workspace, "query_proj")
     check(lib.mfa_query_proj(ctypes.byref(desc), _ptr(x), _ptr(w_qdown), _ptr(w_qup),
                              _ptr(gain), _ptr(q_out), _ptr(ws), ctypes.c_size_t(ws_bytes),
                              _stream(x, stream)))

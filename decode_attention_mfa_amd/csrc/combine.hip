@@ -6,14 +6,20 @@
 // The exact result over the union of the chunks is
 //     M = max_c m_c,  out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
 // (softmax is invariant to the reference max; the chunks partition the keys).
-// One wave per (slot, head); lane l owns channels 4l .. 4l+3.  Splits are
-// merged in increasing order, so the result depends only on the split count.
+// A split without keys leaves m_c = -inf and contributes nothing (its O_c is
+// never read into the sum); a slot without keys gets zeros.
+//
+// One wave per (slot, head); lane l owns channels 4l .. 4l+3.  Every load of
+// a row (all splits' m, l and O) is issued before the first use, so the
+// kernel costs one memory round trip; splits are merged in increasing order,
+// so the result depends only on the split count.
 #include "device_common.h"
 #include "kernel_params.h"
 
 namespace mfa {
 namespace {
 
+template <int kMaxSplits>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p, int group, int d) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // over B*Hkv*G
@@ -23,34 +29,76 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p, int group,
   const int h = (int)(row - bg * group);
   const int b = (int)(bg / p.hkv);
   const int g = (int)(bg - (int64_t)b * p.hkv);
-  const int L = p.ctx_lens[b];
-  const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
-  const int n_tiles = L > 0 ? (L - 1) / kPage - lo / kPage + 1 : 0;
-  const int n_active = min(p.splits, (n_tiles + p.chunk_tiles - 1) / p.chunk_tiles);
-  const int ch = lane * 4;
-  if (ch >= d) return;
+  const int ch = min(lane * 4, d - 4);   // lanes past d re-read the last channels, store nothing
+  const int64_t base = bg * p.splits;
 
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  float inv = 0.f;
-  if (n_active > 0) {
-    const int64_t base = bg * p.splits;
-    float M = kNegInf;
-    for (int s = 0; s < n_active; ++s) M = fmaxf(M, p.part_ml[((base + s) * group + h) * 2]);
-    float lsum = 0.f;
-    for (int s = 0; s < n_active; ++s) {
-      const int64_t r = (base + s) * group + h;
-      const float w = fast_exp2(p.part_ml[r * 2] - M);
-      lsum += w * p.part_ml[r * 2 + 1];
-      acc += w * *reinterpret_cast<const floatx4*>(p.part_o + r * d + ch);
-    }
-    inv = (p.v_scale ? p.v_scale[g] : 1.f) / lsum;
+  floatx2 ml[kMaxSplits];
+  floatx4 o[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int64_t r = (base + min(s, p.splits - 1)) * group + h;
+    ml[s] = *reinterpret_cast<const floatx2*>(p.part_ml + r * 2);
+    o[s] = *reinterpret_cast<const floatx4*>(p.part_o + r * d + ch);
   }
+  float M = kNegInf;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < p.splits) M = fmaxf(M, ml[s].x);
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < p.splits && ml[s].x != kNegInf) {
+      const float w = fast_exp2(ml[s].x - M);
+      lsum += w * ml[s].y;
+      acc += w * o[s];
+    }
+  }
+  const float inv = lsum > 0.f ? (p.v_scale ? p.v_scale[g] : 1.f) / lsum : 0.f;
+  if (lane * 4 >= d) return;
   const floatx4 v = acc * inv;
-  const int64_t o = ((int64_t)b * p.hq + (int64_t)g * group + h) * d + ch;
+  const int64_t off = ((int64_t)b * p.hq + (int64_t)g * group + h) * d + ch;
   if (p.out_f32)
-    *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = v;
+    *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + off) = v;
   else
-    *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) =
+    *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + off) =
+        intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
+}
+
+// Any split count: a running (online) merge, one split at a time.
+__global__ void __launch_bounds__(256) combine_any_kernel(DecodeParams p, int group, int d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nrows = (int64_t)p.batch * p.hkv * group;
+  if (row >= nrows) return;
+  const int64_t bg = row / group;
+  const int h = (int)(row - bg * group);
+  const int b = (int)(bg / p.hkv);
+  const int g = (int)(bg - (int64_t)b * p.hkv);
+  const int ch = min(lane * 4, d - 4);
+  const int64_t base = bg * p.splits;
+  float M = kNegInf, lsum = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.splits; ++s) {
+    const int64_t r = (base + s) * group + h;
+    const floatx2 ml = *reinterpret_cast<const floatx2*>(p.part_ml + r * 2);
+    if (ml.x == kNegInf) continue;
+    const floatx4 os = *reinterpret_cast<const floatx4*>(p.part_o + r * d + ch);
+    const float m_new = fmaxf(M, ml.x);
+    const float a = M == kNegInf ? 0.f : fast_exp2(M - m_new);
+    const float w = fast_exp2(ml.x - m_new);
+    lsum = a * lsum + w * ml.y;
+    acc = a * acc + w * os;
+    M = m_new;
+  }
+  const float inv = lsum > 0.f ? (p.v_scale ? p.v_scale[g] : 1.f) / lsum : 0.f;
+  if (lane * 4 >= d) return;
+  const floatx4 v = acc * inv;
+  const int64_t off = ((int64_t)b * p.hq + (int64_t)g * group + h) * d + ch;
+  if (p.out_f32)
+    *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + off) = v;
+  else
+    *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + off) =
         intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
 }
 
@@ -58,8 +106,15 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p, int group,
 
 hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.hkv * group;
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, p, group, d);
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (p.splits <= 2)
+    hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, p, group, d);
+  else if (p.splits <= 4)
+    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, p, group, d);
+  else if (p.splits <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, p, group, d);
+  else
+    hipLaunchKernelGGL(combine_any_kernel, grid, block, 0, stream, p, group, d);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(kThreads) f32_decode_kernel(DecodeParams p, in
   const int h = blockIdx.x;
   const int group = p.hq / p.hkv;
   const int g = h / group;
-  const int L = p.ctx_lens[b];
+  const int L = slot_len(p.ctx_lens[b], p.max_blocks);
   const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
   const float* q = static_cast<const float*>(p.q) + ((int64_t)b * p.hq + h) * d;
   const float* kpool = static_cast<const float*>(p.k);
@@ -56,7 +56,7 @@ __global__ void __launch_bounds__(kThreads) f32_decode_kernel(DecodeParams p, in
     if (j < L) {
       const float* krow;
       if (p.block_table) {
-        const int64_t blk = p.block_table[(int64_t)b * p.max_blocks + j / kPage];
+        const int64_t blk = pool_block(p.block_table[(int64_t)b * p.max_blocks + j / kPage], p.num_blocks);
         krow = kpool + blk * p.k_block_stride + (int64_t)g * p.k_head_stride + (int64_t)(j % kPage) * p.k_row_stride;
       } else {
         krow = kpool + ((int64_t)b * p.max_blocks + j / kPage) * p.k_block_stride +
@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(kThreads) f32_decode_kernel(DecodeParams p, in
         const int jk = j0 + jj;
         float v;
         if (p.block_table) {
-          const int64_t blk = p.block_table[(int64_t)b * p.max_blocks + jk / kPage];
+          const int64_t blk = pool_block(p.block_table[(int64_t)b * p.max_blocks + jk / kPage], p.num_blocks);
           v = vpool[blk * p.v_block_stride + (int64_t)g * p.v_head_stride + (int64_t)t * p.v_row_stride + jk % kPage];
         } else {
           v = vpool[(int64_t)b * p.v_seq_stride + (int64_t)g * p.v_head_stride + (int64_t)t * p.v_row_stride + jk];

@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
   const int b = bg / p.hkv;
   const int g = bg - b * p.hkv;
   const int split = blockIdx.x;
-  const int L = p.ctx_lens[b];
+  const int L = slot_len(p.ctx_lens[b], p.max_blocks);
   const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
   int n_tiles = 0, t_lo = 0;
   if (L > 0) {
@@ -96,6 +96,9 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
         else
           *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
       }
+    } else if (wave == 0 && q4 == 0) {   // no keys in this split: an empty partial
+      const int64_t row = ((int64_t)bg * p.splits + split) * kG + r;
+      *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{kNegInf, 0.f};
     }
     return;
   }
@@ -105,7 +108,7 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
   const float v_scale = p.v_scale ? p.v_scale[g] : 1.f;
 
   for (int i = threadIdx.x; i < nt; i += 256)
-    blk_ids[i] = p.block_table ? p.block_table[(int64_t)b * p.max_blocks + t_begin + i] : 0;
+    blk_ids[i] = p.block_table ? pool_block(p.block_table[(int64_t)b * p.max_blocks + t_begin + i], p.num_blocks) : 0;
 
   // Q fragments: head r of the group, channels 32s + 8q4 .. +7.
   intx4 qf[D / 32];

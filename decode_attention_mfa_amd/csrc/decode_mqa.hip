@@ -61,7 +61,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool kSplitP>
+template <bool kDense>
 __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing * kPhaseBytes];
   __shared__ int blk_ids[kMaxChunkTiles];
@@ -78,32 +78,19 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
   const int b = bg / p.hkv;
   const int g = bg - b * p.hkv;
   const int split = blockIdx.x;
-  const int L = p.ctx_lens[b];
-  const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
-  int n_tiles = 0, t_lo = 0;
-  if (L > 0) {
-    t_lo = lo / kPage;
-    n_tiles = (L - 1) / kPage - t_lo + 1;
-  }
-  const int t_begin = t_lo + split * p.chunk_tiles;
-  const int t_end = min(t_lo + n_tiles, t_begin + p.chunk_tiles);
   const int head = g * kG + hg * 16 + r;    // this lane's query head
-
-  if (t_begin >= t_end) {
-    if (p.splits == 1 && kh == 0) {  // empty slot: zeros
-      for (int ct = 0; ct < kD / 16; ++ct) {
-        const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
-        if (p.out_f32)
-          *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
-        else
-          *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
-      }
-    }
-    return;
-  }
-  const int nt = t_end - t_begin;
-  const int nphase = 2 * nt;
   const float qk_scale = p.scale * kLog2e;   // bf16 cache: no dequantisation scales
+  const int32_t* trow = p.block_table ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
+
+  // Dense attention: the split's first page (split * chunk) does not depend
+  // on the slot length, so its block id is fetched together with the length
+  // and its K/V loads are in flight before the length is known (a split that
+  // turns out to be past the end simply drops them).  With a window the
+  // first page moves with the length.
+  int t_begin = kDense ? min(split * p.chunk_tiles, p.max_blocks - 1) : 0;
+  const int blk_spec = (kDense && trow) ? trow[t_begin] : 0;
+  const int L = slot_len(p.ctx_lens[b], p.max_blocks);
+  int nphase = 0;   // two phases (K, V) per tile of this split; set once L is known
 
   const uint16_t* kpool = static_cast<const uint16_t*>(p.k);
   const uint16_t* vpool = static_cast<const uint16_t*>(p.v);
@@ -179,24 +166,54 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
     }
   };
 
-  // Start-up order matters: vector loads complete in issue order, so the
-  // block-id cache loads go first, then phases 0 and 1 (their block id comes
-  // straight from the table), then Q; only LDS is fenced before the loop.
-  // (Loads are issued unconditionally, indices clamped: the compiler's wait
-  // counts stay exact only when every path issues the same loads.)
-  const int32_t* btab = p.block_table ? p.block_table + (int64_t)b * p.max_blocks + t_begin
-                                      : static_cast<const int32_t*>(p.ctx_lens);
-  const int blk0_raw = btab[0];
+  intx4 stage0[kPerThread], stage1[kPerThread];
+  auto load_first = [&](int blk) {
+    const int blk0 = pool_block(readfirstlane(blk), p.num_blocks);
+    load_phase(0, stage0, blk0);
+    load_phase(1, stage1, blk0);
+  };
+  if (kDense) load_first(blk_spec);
+
+  const int lo = (!kDense && L > p.window) ? L - p.window : 0;
+  int n_tiles = 0, t_lo = 0;
+  if (L > 0) {
+    t_lo = lo / kPage;
+    n_tiles = (L - 1) / kPage - t_lo + 1;
+  }
+  if (!kDense) t_begin = t_lo + split * p.chunk_tiles;
+  const int t_end = min(t_lo + n_tiles, t_begin + p.chunk_tiles);
+
+  if (t_begin >= t_end || (kDense && split * p.chunk_tiles >= p.max_blocks)) {
+    if (kh == 0) {
+      if (p.splits == 1) {   // empty slot: zeros
+        for (int ct = 0; ct < kD / 16; ++ct) {
+          const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
+          if (p.out_f32)
+            *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
+          else
+            *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
+        }
+      } else if (q4 == 0) {  // no keys in this split: an empty partial for the merge
+        const int64_t row = ((int64_t)bg * p.splits + split) * kG + hg * 16 + r;
+        *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{kNegInf, 0.f};
+      }
+    }
+    return;
+  }
+  const int nt = t_end - t_begin;
+  nphase = 2 * nt;
+
+  // Start-up order: phases 0 and 1 are in flight (dense) or go first, then the
+  // block-id cache (rows t_begin .. t_end-1 of the table), then Q; only LDS
+  // is fenced before the loop.  (Loads are issued unconditionally, indices
+  // clamped: the compiler's wait counts stay exact only when every path
+  // issues the same loads.)
+  if (!kDense) load_first(trow ? trow[t_begin] : 0);
+  const int32_t* btab = trow ? trow + t_begin : static_cast<const int32_t*>(p.ctx_lens);
   int blk_cache[(kMaxChunkTiles + kThreads - 1) / kThreads];
 #pragma unroll
   for (int k = 0; k < (kMaxChunkTiles + kThreads - 1) / kThreads; ++k)
-    blk_cache[k] = btab[p.block_table ? min(tid + k * kThreads, nt - 1) : 0];
-  intx4 stage0[kPerThread], stage1[kPerThread];
-  {
-    const int blk0 = readfirstlane(blk0_raw);
-    load_phase(0, stage0, blk0);
-    load_phase(1, stage1, blk0);
-  }
+    blk_cache[k] = btab[trow ? min(tid + k * kThreads, nt - 1) : 0];
   // Q fragments (B operand of S^T): this lane's head, channels 32s + 8q4 .. +7.
   intx4 qf[kD / 32];
   {
@@ -207,7 +224,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
 #pragma unroll
   for (int k = 0; k < (kMaxChunkTiles + kThreads - 1) / kThreads; ++k) {
     const int i = tid + k * kThreads;
-    if (i < nt) blk_ids[i] = blk_cache[k];
+    if (i < nt) blk_ids[i] = pool_block(blk_cache[k], p.num_blocks);
   }
   store_phase(0, stage0);
   lds_barrier();   // block ids and phase 0 visible
@@ -224,7 +241,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
   floatx4 acc[kD / 16];
 #pragma unroll
   for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-  intx4 pb, pl;
+  intx4 pb;
 
   auto k_phase = [&](const uint8_t* buf, int key0) {
     floatx4 st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -276,13 +293,6 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
     // P^T B operand (keys 8q4 .. 8q4+7 of the half).
     pb = intx4{(int)pack_bf16x2(sv[0][0], sv[0][1]), (int)pack_bf16x2(sv[0][2], sv[0][3]),
                (int)pack_bf16x2(sv[1][0], sv[1][1]), (int)pack_bf16x2(sv[1][2], sv[1][3])};
-    if (kSplitP) {
-      const uint32_t h0 = pb.x, h1 = pb.y, h2 = pb.z, h3 = pb.w;
-      pl = intx4{(int)pack_bf16x2(sv[0][0] - bf16_lo_to_f32(h0), sv[0][1] - bf16_hi_to_f32(h0)),
-                 (int)pack_bf16x2(sv[0][2] - bf16_lo_to_f32(h1), sv[0][3] - bf16_hi_to_f32(h1)),
-                 (int)pack_bf16x2(sv[1][0] - bf16_lo_to_f32(h2), sv[1][1] - bf16_hi_to_f32(h2)),
-                 (int)pack_bf16x2(sv[1][2] - bf16_lo_to_f32(h3), sv[1][3] - bf16_hi_to_f32(h3))};
-    }
   };
 
   auto v_phase = [&](const uint8_t* buf) {
@@ -291,7 +301,6 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
     for (int ct = 0; ct < kD / 16; ++ct) {
       const intx4 a = *reinterpret_cast<const intx4*>(buf + ct * 2048 + r * 128 + chunk * 16);
       acc[ct] = mfma_bf16_16x16x32(a, pb, acc[ct]);
-      if (kSplitP) acc[ct] = mfma_bf16_16x16x32(a, pl, acc[ct]);
     }
   };
 
@@ -371,9 +380,9 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
 
 }  // namespace
 
-hipError_t launch_mqa_bf16(const DecodeParams& p, bool split_p, hipStream_t stream) {
+hipError_t launch_mqa_bf16(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(p.splits, p.batch * p.hkv);
-  if (split_p)
+  if (p.window == 0)
     hipLaunchKernelGGL(mqa_decode_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(mqa_decode_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, p);

@@ -47,6 +47,20 @@ __device__ __forceinline__ intx2 e4m3x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// A cache block id from the block table, kept inside the pool: ids outside
+// [0, num_blocks) (a caller error, or table entries past a slot's end that
+// are fetched ahead of time) read block 0 instead of faulting.
+__device__ __forceinline__ int pool_block(int blk, int64_t num_blocks) {
+  return (int64_t)(uint32_t)blk < num_blocks ? blk : 0;
+}
+
+// A slot length kept inside [0, max_blocks * 64] (a longer or negative
+// length is a caller error; clamping keeps every table and cache read in
+// bounds).
+__device__ __forceinline__ int slot_len(int L, int max_blocks) {
+  return min(max(L, 0), max_blocks * 64);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-byte global -> LDS copy without a register round trip

@@ -6,19 +6,15 @@
 
 namespace mfa {
 
-constexpr int kPage = 64;          // tokens per cache block
-constexpr int kTile = 32;          // keys per pipeline tile (half a block)
-constexpr int kTilesPerPage = kPage / kTile;
-
-enum class KvType : int { F32 = 0, BF16 = 1, FP8 = 2 };
+constexpr int kPage = 64;          // tokens per cache block (one kernel tile)
 
 // One decode-attention launch.  Element strides are in elements of the KV
-// storage type.  For a paged cache the K/V tile of (slot b, tile t, group g)
-// starts at   k + block * k_block_stride + g * k_head_stride + (t % 2) * 32 * k_row_stride
-//             v + block * v_block_stride + g * v_head_stride + (t % 2) * 32
-// with block = block_table[b * max_blocks + t / 2]; for a contiguous cache
-// the block index is replaced by (b * max_blocks + t / 2) for K and the V tile
-// starts at v + b * v_seq_stride + g * v_head_stride + t * 32.
+// storage type.  For a paged cache the K/V tile of (slot b, page t, group g)
+// starts at   k + block * k_block_stride + g * k_head_stride
+//             v + block * v_block_stride + g * v_head_stride
+// with block = block_table[b * max_blocks + t]; for a contiguous cache the
+// block index is replaced by (b * max_blocks + t) for K and the V tile starts
+// at v + b * v_seq_stride + g * v_head_stride + t * 64.
 struct DecodeParams {
   const void* q;              // [B, Hq, d]
   const void* k;
@@ -35,6 +31,7 @@ struct DecodeParams {
   int32_t hq;
   int32_t hkv;
   int32_t max_blocks;         // block-table row length / capacity in blocks
+  int64_t num_blocks;         // blocks in the paged pool (ids are clamped into it)
   int32_t window;             // 0 = dense
   int32_t splits;             // >= 1
   int32_t chunk_tiles;        // 32-key tiles per split

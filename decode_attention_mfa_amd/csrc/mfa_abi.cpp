@@ -9,7 +9,7 @@
 #include "kernel_params.h"
 
 namespace mfa {
-hipError_t launch_mqa_bf16(const DecodeParams& p, bool split_p, hipStream_t stream);
+hipError_t launch_mqa_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gqa(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_f32(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream);
@@ -63,6 +63,7 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
   p.hq = d->num_q_heads;
   p.hkv = d->num_kv_heads;
   p.max_blocks = d->max_blocks_per_seq;
+  p.num_blocks = d->num_blocks;
   p.window = window;
   p.splits = pl.splits;
   p.chunk_tiles = pl.chunk_pages;
@@ -101,6 +102,7 @@ mfa_status decode_impl(const mfa_decode_desc* d, const void* q, const void* k_ca
   if (st != MFA_OK) return st;
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) % mfa::kWorkspaceAlign))
     return MFA_ERR_ALIGN;
+  if (block_table && d->num_blocks <= 0) return MFA_ERR_SHAPE;   // a paged call needs a pool
   int cus = 0;
   if (d->num_splits == 0) {
     cus = device_cu_count();
@@ -116,7 +118,7 @@ mfa_status decode_impl(const mfa_decode_desc* d, const void* q, const void* k_ca
   hipError_t e = hipSuccess;
   switch (pl.path) {
     case mfa::DecodePath::kMqaShared:
-      e = mfa::launch_mqa_bf16(p, /*split_p=*/false, s);
+      e = mfa::launch_mqa_bf16(p, s);
       break;
     case mfa::DecodePath::kGqaSplitKeys:
       e = mfa::launch_gqa(p, d->head_dim, s);

@@ -45,7 +45,9 @@
  * Errors
  *   Problems detectable on the host return a non-zero mfa_status and enqueue
  *   nothing.  Device-side contract violations (a block id outside the pool,
- *   L > max_blocks_per_seq * P, L < 0) are undefined behaviour.
+ *   L > max_blocks_per_seq * P, L < 0) give unspecified values for that
+ *   slot but never an out-of-bounds access: ids outside [0, num_blocks)
+ *   read block 0 and lengths are clamped into [0, max_blocks_per_seq * P].
  */
 #ifndef MFA_DECODE_H
 #define MFA_DECODE_H
@@ -89,8 +91,8 @@ typedef enum mfa_dtype {
  *   page_size           tokens per cache block; must be 64
  *   max_blocks_per_seq  paged: length (= row stride) of each block-table row;
  *                       contiguous: cache capacity / 64
- *   num_blocks          paged: blocks in each pool (documentation / checks
- *                       only); contiguous: ignored
+ *   num_blocks          paged: blocks in each pool (>= 1; block ids are
+ *                       clamped into it); contiguous: ignored
  *   q_dtype, kv_dtype, out_dtype
  *                       supported: kv BF16 or FP8_E4M3 with q BF16 and out
  *                       BF16 or F32; kv F32 with q F32 and out F32
