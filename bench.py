@@ -42,19 +42,24 @@ WORKLOADS = {
 
 
 def make_case(config):
+    """Host-drawn inputs for configs 2-4; the Step-5 layer (5: global, 6: local
+    window) is drawn on the device (its 1.6 GB pool takes minutes on the host)."""
     from workloads import config_case
     if config in (2, 3, 4):
         return config_case(config, nan_tail=False)
-    if config == 5:
-        return config_case(5, window=0, nan_tail=False)
-    if config == 6:
-        return config_case(5, window=512, nan_tail=False)
+    if config in (5, 6):
+        from workloads.device_gen import make_device_case
+        return make_device_case(5, batch=32, ctx_lens=[32768] * 32, hq=64, hkv=4, d=192,
+                                window=512 if config == 6 else 0, nan_tail=False,
+                                name=f"c{config}")
     raise SystemExit(f"unknown --config {config}")
 
 
 def cpu_baseline(case, budget_s):
-    """The oracle as it stands, on the host cores, over as many slots of the
-    same workload as fit in about budget_s seconds."""
+    """The oracle as it stands, on the host cores: it evaluates the slots of
+    the same workload one after another (cycling through the batch) until
+    about budget_s seconds have passed; one slot evaluation is one query
+    token's decode-attention step."""
     from threadpoolctl import threadpool_info
     from oracle import decode_attention
     q = case.q
@@ -65,16 +70,69 @@ def cpu_baseline(case, budget_s):
     kw = case.oracle_kwargs()
     done = 0
     t0 = time.perf_counter()
-    while done < case.batch and (time.perf_counter() - t0) < budget_s:
+    while (time.perf_counter() - t0) < budget_s:
         decode_attention(q, case.k_cache, case.v_cache, case.ctx_lens, case.scale,
-                         slots=[done], **kw)
+                         slots=[done % case.batch], **kw)
         done += 1
     el = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": done / el, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {case.batch} slots of the same workload ({case.name}), "
-                      f"fp64 numpy oracle, {el:.1f} s",
+            "sample": f"{done} slot evaluations ({done / case.batch:.1f} passes over the "
+                      f"{case.batch} slots of the same workload), fp64 numpy oracle, {el:.1f} s",
             "host_cpu_count": os.cpu_count()}
+
+
+# Sources whose change invalidates the committed counter summary.
+TRAFFIC_SOURCES = ["decode_mqa.hip", "decode_gqa.hip", "combine.hip", "device_common.h",
+                   "kernel_params.h", "host_plan.cpp"]
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_mfa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# Committed rocprofv3 counter summaries, by --config.
+COUNTER_SUMMARIES = {2: "mqa_decode_b64_l4096_bf16_counters.txt"}
+
+
+def committed_traffic(config):
+    """HBM bytes per call from the committed rocprofv3 counter summary of this
+    workload, or None when there is none or the kernels changed since."""
+    name = COUNTER_SUMMARIES.get(config)
+    path = os.path.join(ROOT, "profiles", name) if name else ""
+    if not name or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(steps):
+    """A plain device-to-device copy of a known size (1 GiB per dispatch), run
+    under rocprofv3 --pmc to scale the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": steps}), flush=True)
 
 
 def main():
@@ -87,12 +145,18 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the decode path shards by slot with no cross-GPU traffic, so run one "
               "process per GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     import torch
     import decode_attention_mfa_amd as mfa
@@ -104,7 +168,14 @@ def main():
     torch.cuda.set_device(dev)
     log(f"bench: building config {args.config} inputs")
     case = make_case(args.config)
-    t = to_device(case, device=dev)
+    if hasattr(case, "host_slots"):   # drawn on the device
+        t = {"q": case.q, "k": case.k, "v": case.v, "table": case.table, "lens": case.lens,
+             "k_scale": None, "v_scale": None,
+             "out": torch.empty((case.batch, case.hq, case.d), dtype=torch.bfloat16, device=dev)}
+        cpu_case = case.host_slots([0, 1])
+    else:
+        t = to_device(case, device=dev)
+        cpu_case = case
     if t["q"] is None:   # FP8 config without the query path: draw q (bf16) on the host
         from workloads import bf16_round_bits
         rng = np.random.default_rng(404)
@@ -182,12 +253,13 @@ def main():
         "algorithmic_bytes_per_call": nbytes,
         "flops_per_call": flops,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "timed": "HIP events around each call on the launch stream"},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(args.config),
+                     "timed": "HIP events around each call (attention kernel + split merge "
+                              "kernel) on the launch stream"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample of the same workload")
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cpu_case, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
