@@ -30,6 +30,8 @@
 // when a tile's max exceeds it by more than kLazyRescale (2^8 headroom for
 // p = 2^(s - m) in fp32/bf16), so O is rescaled a handful of times per split;
 // the algebra is unchanged.  P is rounded to bf16 for the PV operand.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernel_params.h"
 
@@ -39,9 +41,8 @@ namespace {
 constexpr int kD = 256;
 constexpr int kG = 64;
 constexpr int kThreads = 512;
-constexpr int kPhaseBytes = 32768;
+constexpr int kPhaseBytes = 32768;   // one bf16 K or V^T tile in LDS
 constexpr int kRing = 3;
-constexpr int kPerThread = kPhaseBytes / 16 / kThreads;   // 16-byte chunks per thread per phase
 constexpr int kMaxChunkTiles = 2048;   // block ids cached per workgroup
 constexpr float kLazyRescale = 8.f;    // log2 headroom before the max moves
 
@@ -61,8 +62,34 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool kDense>
-__global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams p) {
+// Converts 16 E4M3 codes (one 16-byte chunk) to two 16-byte bf16 chunks.
+// Every E4M3FN value is a bf16 value, and the conversion scale is 1, so this
+// is exact (NaN codes stay NaN).
+template <bool kUpper>
+__device__ __forceinline__ int e4m3x2_to_bf16x2(int w) {   // codes of bytes 0,1 (or 2,3)
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kUpper));
+}
+__device__ __forceinline__ void e4m3x16_to_bf16(intx4 raw, intx4& lo, intx4& hi) {
+  lo = intx4{e4m3x2_to_bf16x2<false>(raw.x), e4m3x2_to_bf16x2<true>(raw.x),
+             e4m3x2_to_bf16x2<false>(raw.y), e4m3x2_to_bf16x2<true>(raw.y)};
+  hi = intx4{e4m3x2_to_bf16x2<false>(raw.z), e4m3x2_to_bf16x2<true>(raw.z),
+             e4m3x2_to_bf16x2<false>(raw.w), e4m3x2_to_bf16x2<true>(raw.w)};
+}
+
+// kDense: no window (the split's first page is known before the length).
+// kFp8: the cache holds OCP E4M3 codes with one fp32 scale per KV head; tiles
+// are converted to bf16 as they are written to LDS, and the scales are
+// applied to the logits (k) and to the normalised output (v).
+template <bool kDense, bool kFp8>
+__global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
+  constexpr int kElem = kFp8 ? 1 : 2;                 // bytes per cached element
+  constexpr int kPerThread = kPhaseBytes * kElem / 2 / 16 / kThreads;   // 16-byte loads per phase
+  // Register stages: phases in flight while a phase is computed (3 bf16
+  // phases = 96 KB of cache data per CU; 4 FP8 phases = 64 KB, as many as
+  // the conversion temporaries leave registers for).
+  constexpr int kStages = kFp8 ? 4 : 3;
+  constexpr int kUnroll = kStages == 3 ? 6 : 4;    // steps per unrolled group: kStages | kUnroll, 2 | kUnroll
+  constexpr int kFirstTiles = (kStages + 1) / 2;   // tiles the start-up loads touch
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing * kPhaseBytes];
   __shared__ int blk_ids[kMaxChunkTiles];
   __shared__ float half_ml[4][16][2];
@@ -79,7 +106,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
   const int g = bg - b * p.hkv;
   const int split = blockIdx.x;
   const int head = g * kG + hg * 16 + r;    // this lane's query head
-  const float qk_scale = p.scale * kLog2e;   // bf16 cache: no dequantisation scales
+  const float qk_scale = p.scale * kLog2e * (kFp8 ? p.k_scale[g] : 1.f);
   const int32_t* trow = p.block_table ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
 
   // Dense attention: the split's first page (split * chunk) does not depend
@@ -88,47 +115,58 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
   // turns out to be past the end simply drops them).  With a window the
   // first page moves with the length.
   int t_begin = kDense ? min(split * p.chunk_tiles, p.max_blocks - 1) : 0;
-  const int blk_spec = (kDense && trow) ? trow[t_begin] : 0;
+  int blk_first[kFirstTiles];
+#pragma unroll
+  for (int i = 0; i < kFirstTiles; ++i)
+    blk_first[i] = (kDense && trow) ? trow[min(t_begin + i, p.max_blocks - 1)] : 0;
   const int L = slot_len(p.ctx_lens[b], p.max_blocks);
   int nphase = 0;   // two phases (K, V) per tile of this split; set once L is known
 
-  const uint16_t* kpool = static_cast<const uint16_t*>(p.k);
-  const uint16_t* vpool = static_cast<const uint16_t*>(p.v);
-  // This thread's chunks of a phase: idx = tid + 512 k, i.e. rows
-  // (tid >> 5) + 16k of a K tile (32 chunks per row) and rows (tid >> 3) + 64k
-  // of a V^T tile (8 chunks per row).  The V^T swizzle repeats every 16 rows,
-  // the K swizzle every 32: odd k flip bit 3 of the K chunk index.
-  const int krow0 = tid >> 5, kc = tid & 31;
-  const int vrow0 = tid >> 3, vc = tid & 7;
-  const int32_t kgoff0 = krow0 * (int32_t)p.k_row_stride + kc * 8;
-  const int32_t vgoff0 = vrow0 * (int32_t)p.v_row_stride + vc * 8;
+  const char* kpool = static_cast<const char*>(p.k);
+  const char* vpool = static_cast<const char*>(p.v);
+  // This thread's 16-byte chunks of a phase, idx = tid + 512 k.
+  //  bf16: rows (tid >> 5) + 16k of a K tile (32 chunks per row), rows
+  //        (tid >> 3) + 64k of a V^T tile (8 chunks per row).  The V^T
+  //        swizzle repeats every 16 rows, the K swizzle every 32: odd k flip
+  //        bit 3 of the K chunk index.
+  //  FP8:  rows (tid >> 4) + 32k of a K tile (16 code chunks per row) and
+  //        rows (tid >> 2) + 128k of a V^T tile (4 per row); code chunk c
+  //        becomes bf16 chunks 2c and 2c + 1 of the same LDS row, and the
+  //        row steps keep the swizzle.
+  const int krow0 = kFp8 ? tid >> 4 : tid >> 5, kc = kFp8 ? tid & 15 : tid & 31;
+  const int vrow0 = kFp8 ? tid >> 2 : tid >> 3, vc = kFp8 ? tid & 3 : tid & 7;
+  const int64_t kgoff0 = ((int64_t)krow0 * p.k_row_stride + kc * (16 / kElem)) * kElem;
+  const int64_t vgoff0 = ((int64_t)vrow0 * p.v_row_stride + vc * (16 / kElem)) * kElem;
+  const int64_t kgstep = (int64_t)(kFp8 ? 32 : 16) * p.k_row_stride * kElem;
+  const int64_t vgstep = (int64_t)(kFp8 ? 128 : 64) * p.v_row_stride * kElem;
   const uint32_t klds_even = krow0 * 512 + ((kc ^ swz_k(krow0)) << 4);
   const uint32_t klds_odd = krow0 * 512 + ((kc ^ swz_k(krow0 + 16)) << 4);
   const uint32_t vlds0 = vrow0 * 128 + ((vc ^ swz_v(vrow0)) << 4);
+  const uint32_t k8_lo = krow0 * 512 + (((2 * kc) ^ swz_k(krow0)) << 4);
+  const uint32_t k8_hi = krow0 * 512 + (((2 * kc + 1) ^ swz_k(krow0)) << 4);
+  const uint32_t v8_lo = vrow0 * 128 + (((2 * vc) ^ swz_v(vrow0)) << 4);
+  const uint32_t v8_hi = vrow0 * 128 + (((2 * vc + 1) ^ swz_v(vrow0)) << 4);
 
   // Register-staged loads of one phase (nothing past the end of the split).
   // The first two phases take their block ids straight from the table, so
   // they are in flight before the id cache in LDS is filled.
   auto load_phase = [&](int ph, intx4* st, int blk) {
-    const int tile = t_begin + (ph >> 1);
+    const int tile = min(t_begin + (ph >> 1), p.max_blocks - 1);   // start-up loads run ahead
     if ((ph & 1) == 0) {
-      const uint16_t* base =
-          (p.block_table ? kpool + (int64_t)blk * p.k_block_stride
-                         : kpool + ((int64_t)b * p.max_blocks + tile) * p.k_block_stride) +
-          (int64_t)g * p.k_head_stride;
+      const char* base =
+          kpool + ((p.block_table ? (int64_t)blk : (int64_t)b * p.max_blocks + tile) * p.k_block_stride +
+                   (int64_t)g * p.k_head_stride) * kElem + kgoff0;
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k)
-        st[k] = __builtin_nontemporal_load(
-            reinterpret_cast<const intx4*>(base + kgoff0 + k * 16 * (int32_t)p.k_row_stride));
+        st[k] = __builtin_nontemporal_load(reinterpret_cast<const intx4*>(base + k * kgstep));
     } else {
-      const uint16_t* base =
-          (p.block_table ? vpool + (int64_t)blk * p.v_block_stride
-                         : vpool + (int64_t)b * p.v_seq_stride + (int64_t)tile * kPage) +
-          (int64_t)g * p.v_head_stride;
+      const char* base =
+          vpool + ((p.block_table ? (int64_t)blk * p.v_block_stride
+                                  : (int64_t)b * p.v_seq_stride + (int64_t)tile * kPage) +
+                   (int64_t)g * p.v_head_stride) * kElem + vgoff0;
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k)
-        st[k] = __builtin_nontemporal_load(
-            reinterpret_cast<const intx4*>(base + vgoff0 + k * 64 * (int32_t)p.v_row_stride));
+        st[k] = __builtin_nontemporal_load(reinterpret_cast<const intx4*>(base + k * vgstep));
     }
   };
   auto load_phase_cached = [&](int ph, intx4* st) {
@@ -137,26 +175,51 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
 
   // Publishing a V^T phase also zeroes the keys past the slot end (their
   // cache rows may hold anything, NaN included), so the PV product never
-  // multiplies garbage by a zero probability.  A chunk holds 8 consecutive
-  // keys vc*8 .. vc*8+7 of one channel.
+  // multiplies garbage by a zero probability.  A bf16 chunk holds 8
+  // consecutive keys of one channel (vc*8 .. vc*8+7; FP8: 16 keys vc*16 ..).
+  auto keep_mask = [&](int valid, uint32_t* keep) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      keep[e] = ((2 * e < valid) ? 0x0000ffffu : 0u) | ((2 * e + 1 < valid) ? 0xffff0000u : 0u);
+  };
+  auto apply = [](intx4 v, const uint32_t* keep) {
+    v.x &= keep[0];
+    v.y &= keep[1];
+    v.z &= keep[2];
+    v.w &= keep[3];
+    return v;
+  };
   auto store_phase = [&](int ph, const intx4* st) {
     if (ph >= nphase) return;
     uint8_t* dst = ring + (ph % kRing) * kPhaseBytes;
-    if (ph & 1) {
-      const int valid = L - (t_begin + (ph >> 1)) * kPage - vc * 8;   // keys of this chunk < L
-      uint32_t keep[4];
+    const int key_rel = L - (t_begin + (ph >> 1)) * kPage;   // keys of this tile < L
+    if (kFp8) {
+      if (ph & 1) {
+        uint32_t keep_lo[4], keep_hi[4];
+        keep_mask(key_rel - vc * 16, keep_lo);
+        keep_mask(key_rel - vc * 16 - 8, keep_hi);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        keep[e] = ((2 * e < valid) ? 0x0000ffffu : 0u) | ((2 * e + 1 < valid) ? 0xffff0000u : 0u);
+        for (int k = 0; k < kPerThread; ++k) {
+          intx4 lo, hi;
+          e4m3x16_to_bf16(st[k], lo, hi);
+          *reinterpret_cast<intx4*>(dst + v8_lo + k * 128 * 128) = apply(lo, keep_lo);
+          *reinterpret_cast<intx4*>(dst + v8_hi + k * 128 * 128) = apply(hi, keep_hi);
+        }
+      } else {
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k) {
-        intx4 v = st[k];
-        v.x &= keep[0];
-        v.y &= keep[1];
-        v.z &= keep[2];
-        v.w &= keep[3];
-        *reinterpret_cast<intx4*>(dst + vlds0 + k * 64 * 128) = v;
+        for (int k = 0; k < kPerThread; ++k) {
+          intx4 lo, hi;
+          e4m3x16_to_bf16(st[k], lo, hi);
+          *reinterpret_cast<intx4*>(dst + k8_lo + k * 32 * 512) = lo;
+          *reinterpret_cast<intx4*>(dst + k8_hi + k * 32 * 512) = hi;
+        }
       }
+    } else if (ph & 1) {
+      uint32_t keep[4];
+      keep_mask(key_rel - vc * 8, keep);
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k)
+        *reinterpret_cast<intx4*>(dst + vlds0 + k * 64 * 128) = apply(st[k], keep);
     } else {
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
@@ -166,13 +229,15 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
     }
   };
 
-  intx4 stage0[kPerThread], stage1[kPerThread];
-  auto load_first = [&](int blk) {
-    const int blk0 = pool_block(readfirstlane(blk), p.num_blocks);
-    load_phase(0, stage0, blk0);
-    load_phase(1, stage1, blk0);
+  intx4 stage[kStages][kPerThread];
+  // The first kStages phases, block ids straight from the table (tiles past
+  // the split's end are clamped into the table row and never published).
+  auto load_first = [&]() {
+#pragma unroll
+    for (int ph = 0; ph < kStages; ++ph)
+      load_phase(ph, stage[ph], pool_block(readfirstlane(blk_first[ph >> 1]), p.num_blocks));
   };
-  if (kDense) load_first(blk_spec);
+  if (kDense) load_first();
 
   const int lo = (!kDense && L > p.window) ? L - p.window : 0;
   int n_tiles = 0, t_lo = 0;
@@ -203,12 +268,17 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
   const int nt = t_end - t_begin;
   nphase = 2 * nt;
 
-  // Start-up order: phases 0 and 1 are in flight (dense) or go first, then the
-  // block-id cache (rows t_begin .. t_end-1 of the table), then Q; only LDS
-  // is fenced before the loop.  (Loads are issued unconditionally, indices
-  // clamped: the compiler's wait counts stay exact only when every path
-  // issues the same loads.)
-  if (!kDense) load_first(trow ? trow[t_begin] : 0);
+  // Start-up order: the first kStages phases are in flight (dense) or go
+  // first, then the block-id cache (rows t_begin .. t_end-1 of the table),
+  // then Q; only LDS is fenced before the loop.  (Loads are issued
+  // unconditionally, indices clamped: the compiler's wait counts stay exact
+  // only when every path issues the same loads.)
+  if (!kDense) {
+#pragma unroll
+    for (int i = 0; i < kFirstTiles; ++i)
+      blk_first[i] = trow ? trow[min(t_begin + i, p.max_blocks - 1)] : 0;
+    load_first();
+  }
   const int32_t* btab = trow ? trow + t_begin : static_cast<const int32_t*>(p.ctx_lens);
   int blk_cache[(kMaxChunkTiles + kThreads - 1) / kThreads];
 #pragma unroll
@@ -226,9 +296,11 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
     const int i = tid + k * kThreads;
     if (i < nt) blk_ids[i] = pool_block(blk_cache[k], p.num_blocks);
   }
-  store_phase(0, stage0);
+  store_phase(0, stage[0]);
   lds_barrier();   // block ids and phase 0 visible
-  load_phase_cached(min(2, nphase - 2), stage0);   // (a one-tile split re-loads phase 0; unused)
+  // Phase kStages into the freed stage (clamped to the last tile, same K/V
+  // parity, when the split is shorter; such a copy is never published).
+  load_phase_cached(min(kStages, nphase - 2 + (kStages & 1)), stage[0]);
 
   // K operand row of S^T tile j: key = 32kh + 8(r/4) + 4j + r%4; its swizzle
   // does not depend on j (bit 2 of the key is not used).
@@ -304,33 +376,54 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
     }
   };
 
-  // Step ph: publish phase ph+1 (staged two steps ago) into its slot, start
-  // loading phase ph+3 into the freed registers, barrier, compute phase ph.
-  // Slot ph+1 last held phase ph-2, finished by every wave before the barrier
-  // of step ph-1.  Even steps are K phases, odd steps V phases.
-  auto k_step = [&](int ph, bool more) {
-    store_phase(ph + 1, stage1);              // phase ph+1 was staged in stage1
-    if (more) load_phase_cached(ph + 3, stage1);
+  // Step ph: publish phase ph+1 (loaded kStages steps ago) into its slot,
+  // start loading phase ph+1+kStages into the freed registers, barrier,
+  // compute phase ph.  Slot ph+1 last held phase ph-2, finished by every wave
+  // before the barrier of step ph-1.  Phase q lives in stage q % kStages;
+  // steps are unrolled kUnroll at a time (a multiple of kStages and of the
+  // K/V period), so every stage index is a constant.
+  auto step = [&](auto ic, int ph, bool more) {
+    constexpr int I = decltype(ic)::value;        // ph % kUnroll
+    constexpr int st = (I + 1) % kStages;
+    store_phase(ph + 1, stage[st]);
+    if (more) load_phase_cached(ph + 1 + kStages, stage[st]);
     lds_barrier();
-    k_phase(ring + (ph % kRing) * kPhaseBytes, (t_begin + (ph >> 1)) * kPage);
+    if ((I & 1) == 0)
+      k_phase(ring + (ph % kRing) * kPhaseBytes, (t_begin + (ph >> 1)) * kPage);
+    else
+      v_phase(ring + (ph % kRing) * kPhaseBytes);
   };
-  auto v_step = [&](int ph, bool more) {
-    store_phase(ph + 1, stage0);              // phase ph+1 (next K) was staged in stage0
-    if (more) load_phase_cached(ph + 3, stage0);
-    lds_barrier();
-    v_phase(ring + (ph % kRing) * kPhaseBytes);
-  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
   // Main loop: every load it issues is in range, so the issue pattern (and
   // the compiler's wait counts) is the same in every iteration.
   int ph = 0;
-  for (; ph + 4 < nphase; ph += 2) {
-    k_step(ph, true);
-    v_step(ph + 1, true);
+  for (; ph + kUnroll + kStages < nphase; ph += kUnroll) {
+    step(I0{}, ph, true);
+    step(I1{}, ph + 1, true);
+    step(I2{}, ph + 2, true);
+    step(I3{}, ph + 3, true);
+    if constexpr (kUnroll == 6) {
+      step(I4{}, ph + 4, true);
+      step(I5{}, ph + 5, true);
+    }
   }
-  // Tail: the last one or two tiles.
-  for (; ph < nphase; ph += 2) {
-    k_step(ph, ph + 3 < nphase);
-    v_step(ph + 1, ph + 4 < nphase);
+  // Tail: the last tiles (loads only while in range).
+  for (; ph < nphase; ph += kUnroll) {
+    step(I0{}, ph, ph + 1 + kStages < nphase);
+    step(I1{}, ph + 1, ph + 2 + kStages < nphase);
+    if (ph + 2 >= nphase) break;
+    step(I2{}, ph + 2, ph + 3 + kStages < nphase);
+    step(I3{}, ph + 3, ph + 4 + kStages < nphase);
+    if constexpr (kUnroll == 6) {
+      if (ph + 4 >= nphase) break;
+      step(I4{}, ph + 4, ph + 5 + kStages < nphase);
+      step(I5{}, ph + 5, ph + 6 + kStages < nphase);
+    }
   }
 
   // ---- merge the two key halves of each head group ----
@@ -358,7 +451,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
     acc[ct] = w0 * acc[ct] + w1 * *reinterpret_cast<const floatx4*>(obuf + (hg * 16 + r) * kD + ct * 16 + q4 * 4);
 
   if (p.splits == 1) {
-    const float inv = 1.f / l_tot;
+    const float inv = (kFp8 ? p.v_scale[g] : 1.f) / l_tot;
 #pragma unroll
     for (int ct = 0; ct < kD / 16; ++ct) {
       const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
@@ -380,12 +473,20 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_bf16_kernel(DecodeParams 
 
 }  // namespace
 
-hipError_t launch_mqa_bf16(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream) {
   dim3 grid(p.splits, p.batch * p.hkv);
-  if (p.window == 0)
-    hipLaunchKernelGGL(mqa_decode_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(mqa_decode_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+  const bool dense = p.window == 0;
+  if (fp8) {
+    if (dense)
+      hipLaunchKernelGGL((mqa_decode_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mqa_decode_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (dense)
+      hipLaunchKernelGGL((mqa_decode_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mqa_decode_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

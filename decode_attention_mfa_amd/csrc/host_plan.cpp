@@ -24,11 +24,8 @@ int path_for(int32_t group, int32_t d, int32_t kv) {
   return -1;
 }
 
-// FP8 storage: no kernel yet.
-bool fp8_supported(int path) {
-  (void)path;
-  return false;
-}
+// FP8 storage: the shared-tile MQA kernel converts tiles on the way to LDS.
+bool fp8_supported(int path) { return path == (int)DecodePath::kMqaShared; }
 
 }  // namespace
 

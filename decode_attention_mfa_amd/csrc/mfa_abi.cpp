@@ -9,7 +9,7 @@
 #include "kernel_params.h"
 
 namespace mfa {
-hipError_t launch_mqa_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_gqa(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_f32(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream);
@@ -118,7 +118,7 @@ mfa_status decode_impl(const mfa_decode_desc* d, const void* q, const void* k_ca
   hipError_t e = hipSuccess;
   switch (pl.path) {
     case mfa::DecodePath::kMqaShared:
-      e = mfa::launch_mqa_bf16(p, s);
+      e = mfa::launch_mqa(p, d->kv_dtype == MFA_FP8_E4M3, s);
       break;
     case mfa::DecodePath::kGqaSplitKeys:
       e = mfa::launch_gqa(p, d->head_dim, s);

@@ -71,8 +71,9 @@ def test_null_descriptor_and_pointers():
     assert call_mqa(desc(), q=None) == MFA_ERR_NULL
     assert call_mqa(desc(), out=None) == MFA_ERR_NULL
     assert call_mqa(desc(), lens=None) == MFA_ERR_NULL
-    # FP8 storage has no kernel yet: refused as a dtype before pointers are looked at
-    assert call_mqa(desc(kv_dtype=MFA_FP8_E4M3), ks=A, vs=None) == MFA_ERR_DTYPE
+    # FP8 needs both scales
+    assert call_mqa(desc(kv_dtype=MFA_FP8_E4M3), ks=A, vs=None) == MFA_ERR_NULL
+    assert call_mqa(desc(kv_dtype=MFA_FP8_E4M3), ks=None, vs=A) == MFA_ERR_NULL
 
 
 def test_dtype_combinations():
@@ -90,6 +91,12 @@ def test_shape_rules():
     assert call_mqa(desc(batch=-1)) == MFA_ERR_SHAPE
     assert call_mqa(desc(num_splits=-2)) == MFA_ERR_SHAPE
     assert call_gqa(desc(num_q_heads=64, num_kv_heads=3), 0) == MFA_ERR_SHAPE  # 64 % 3
+
+
+def test_fp8_only_on_the_shared_tile_path():
+    # 16 heads per group (the key-split kernel) has no FP8 variant
+    assert call_gqa(desc(num_q_heads=64, num_kv_heads=4, head_dim=192,
+                         kv_dtype=MFA_FP8_E4M3), 0) == MFA_ERR_DTYPE
 
 
 def test_alignment_scale_window_workspace():

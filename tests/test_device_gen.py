@@ -45,3 +45,23 @@ def test_seeded():
     a, b = _case(), _case()
     assert torch.equal(a.k.view(torch.int16), b.k.view(torch.int16))
     assert np.array_equal(a.block_table, b.block_table)
+
+
+def test_e4m3_scales_and_codes():
+    dc = make_device_case(4, batch=3, ctx_lens=[70, 1, 128], hq=8, hkv=2, d=32,
+                          kv_format="e4m3", device="cpu")
+    assert dc.k.dtype == torch.float8_e4m3fn and dc.k_scale.shape == (2,)
+    codes = dc.k.view(torch.uint8).numpy()
+    last = dc.block_table[0, 1]                                   # slot 0: 70 keys -> 6 rows
+    assert (codes[last, :, 6:, :] == 0x7F).all()
+    valid = []                                                    # every valid row of the pool
+    for b, L in enumerate(dc.ctx_lens):
+        for j in range((int(L) + 63) // 64):
+            rows = min(64, int(L) - 64 * j)
+            valid.append(codes[dc.block_table[b, j], :, :rows, :].reshape(2, -1))
+    valid = np.concatenate(valid, axis=1)
+    assert ((valid & 0x7F) != 0x7F).all()                          # no NaN codes in valid rows
+    assert ((valid & 0x7F) == 0x7E).any(axis=1).all()              # each head's absmax hits 448
+    sub = dc.host_slots([2, 0])
+    assert sub.kv_format == "e4m3" and sub.k_cache.dtype == np.uint8
+    np.testing.assert_array_equal(sub.k_scale, dc.k_scale.numpy())
