@@ -1,30 +1,34 @@
 // MQA decode attention on gfx950: 64 query heads share one K head and one V
 // head of width 256 ("Step-3 is Large yet Affordable", section 2 and
-// Table 1).  Hand-written split-K flash decoding over a bf16 cache.
+// Table 1).  Hand-written split-K flash decoding over a bf16 or FP8 cache.
 //
-// Workgroup = 8 waves (two per SIMD) = one (slot, KV group, split).  Wave w
-// owns heads 16*(w%4) .. +15 and key half w/4 (keys 32*(w/4) .. +31 of every
-// 64-key tile).  The split's keys stream through a ring of three 32 KB LDS
-// slots, one "phase" per slot:
-//   phase 2t   : K tile   [64 keys][256 ch]  bf16, rows 512 B
-//   phase 2t+1 : V^T tile [256 ch][64 keys]  bf16, rows 128 B
-// Each thread stages its share of a phase (four 16-byte non-temporal loads,
-// fully coalesced) in registers two phases ahead and writes it into the
-// swizzled slot one phase ahead, so 64 KB per CU is in flight while the
-// waves compute.  The K/V bytes of a tile reach HBM->LDS once per workgroup
-// and are read from LDS by the four head groups.
+// Workgroup = 8 waves (two per SIMD) = one (slot, KV group, split), split by
+// role:
+//   waves 4..7 (loaders)  stream the split's keys HBM -> registers -> LDS in
+//                          32 KB "phases", kStages phases ahead (16-byte
+//                          non-temporal loads, fully coalesced; FP8 codes are
+//                          widened to bf16 on the way), zeroing V rows past
+//                          the slot end;
+//   waves 0..3 (compute)  each own 16 query heads over every key of a tile.
+// Phase 2t is the K tile [64 keys][256 ch] (rows 512 B) in slot 0, phase
+// 2t+1 the V^T tile [256 ch][64 keys] (rows 128 B) in slot 1.  One barrier
+// per phase: after barrier q the compute waves read phase q while the
+// loaders publish phase q+1 into the other slot (last read before barrier q)
+// and issue the loads of phase q+1+kStages.  Loads, LDS stores and the
+// matrix work of one phase therefore overlap instead of running one after
+// the other in every wave.
 //
-// Products are transposed so the softmax statistics stay in lanes:
-//   S^T[key, head] = K[key, :] . Q^T[:, head]       (MFMA A = K rows from LDS,
+// Products are transposed so the softmax statistics stay in lanes (16x16x32
+// bf16 MFMA, fp32 accumulation):
+//   S^T[key, head] = K[key, :] . Q^T[:, head]       (A = K rows from LDS,
 //                                                    B = Q fragments in VGPRs)
-//   O^T[ch, head] += V^T[ch, key] . P^T[key, head]  (A = V^T from LDS, B = P)
-// With MFMA row r of S^T tile j mapped to key 8(r/4) + 4j + r%4 of the wave's
-// half, the S^T values a lane holds (4 keys x 2 tiles of one head) are exactly
-// the B operand of the PV product: no lane shuffle between the products.  Each
-// lane owns one head: the row max is a 4-lane reduction per tile, the row sum
-// is reduced once at the end, and the two key halves of a head group are
-// merged through LDS (log-sum-exp) before the output or split partial is
-// written.
+//   O^T[ch, head] += V^T[ch, key] . P^T[key, head]  (A = V^T rows from LDS, B = P)
+// Row r of S^T tile j (4 tiles of 16 rows per 64-key page) is key
+// 32(j/2) + 8(r/4) + 4(j%2) + r%4, so the 16 S^T values a lane holds (head
+// l%16) are exactly the B operands of its two 32-key PV steps: no lane
+// shuffle.  The row max is a 4-lane reduction per tile and the row sum is
+// reduced once at the end; a compute wave holds all keys of its heads, so
+// its output (or split partial) is final without any merge between waves.
 //
 // Online softmax in the log2 domain, fp32 state.  The running max only moves
 // when a tile's max exceeds it by more than kLazyRescale (2^8 headroom for
@@ -40,14 +44,16 @@ namespace {
 
 constexpr int kD = 256;
 constexpr int kG = 64;
-constexpr int kThreads = 512;
-constexpr int kPhaseBytes = 32768;   // one bf16 K or V^T tile in LDS
-constexpr int kRing = 3;
+constexpr int kThreads = 512;          // 4 compute waves + 4 loader waves
+constexpr int kLoaders = 256;
+constexpr int kPhaseBytes = 32768;     // one bf16 K or V^T tile in LDS
 constexpr int kMaxChunkTiles = 2048;   // block ids cached per workgroup
 constexpr float kLazyRescale = 8.f;    // log2 headroom before the max moves
 
-// LDS swizzles (XOR on the 16-byte chunk index) so that the 16 lanes reading
-// one MFMA operand hit 16 distinct bank quads (and any 8 consecutive lanes 8).
+// LDS swizzles (XOR on the 16-byte chunk index).  The 16 lanes reading one
+// K operand hold keys {0..3, 8..11, 16..19, 24..27} + const: swz_k gives
+// them 16 distinct bank quads.  A V^T read has 16 lanes on 16 consecutive
+// channels (two per 256-byte bank row).
 __device__ __forceinline__ int swz_k(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
 __device__ __forceinline__ int swz_v(int ch) { return (ch & 7) ^ ((ch >> 3) & 1); }
 
@@ -76,6 +82,24 @@ __device__ __forceinline__ void e4m3x16_to_bf16(intx4 raw, intx4& lo, intx4& hi)
              e4m3x2_to_bf16x2<false>(raw.w), e4m3x2_to_bf16x2<true>(raw.w)};
 }
 
+// Keep masks for a bf16 chunk of 8 consecutive keys of which `valid` (may be
+// <= 0 or >= 8) are below the slot end.
+__device__ __forceinline__ void keep_mask(int valid, uint32_t* keep) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    keep[e] = ((2 * e < valid) ? 0x0000ffffu : 0u) | ((2 * e + 1 < valid) ? 0xffff0000u : 0u);
+}
+__device__ __forceinline__ intx4 apply_keep(intx4 v, const uint32_t* keep) {
+  v.x &= keep[0];
+  v.y &= keep[1];
+  v.z &= keep[2];
+  v.w &= keep[3];
+  return v;
+}
+
+template <int N>
+using Int = std::integral_constant<int, N>;
+
 // kDense: no window (the split's first page is known before the length).
 // kFp8: the cache holds OCP E4M3 codes with one fp32 scale per KV head; tiles
 // are converted to bf16 as they are written to LDS, and the scales are
@@ -83,75 +107,65 @@ __device__ __forceinline__ void e4m3x16_to_bf16(intx4 raw, intx4& lo, intx4& hi)
 template <bool kDense, bool kFp8>
 __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   constexpr int kElem = kFp8 ? 1 : 2;                 // bytes per cached element
-  constexpr int kPerThread = kPhaseBytes * kElem / 2 / 16 / kThreads;   // 16-byte loads per phase
-  // Register stages: phases in flight while a phase is computed (3 bf16
-  // phases = 96 KB of cache data per CU; 4 FP8 phases = 64 KB, as many as
-  // the conversion temporaries leave registers for).
-  constexpr int kStages = kFp8 ? 4 : 3;
-  constexpr int kUnroll = kStages == 3 ? 6 : 4;    // steps per unrolled group: kStages | kUnroll, 2 | kUnroll
-  constexpr int kFirstTiles = (kStages + 1) / 2;   // tiles the start-up loads touch
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing * kPhaseBytes];
+  constexpr int kPerThread = kPhaseBytes * kElem / 2 / 16 / kLoaders;   // 16-byte loads per phase
+  // Phases in flight in the loaders' registers: 4 bf16 or 8 FP8 phases,
+  // 128 KB of cache data per CU either way.
+  constexpr int kStages = kFp8 ? 8 : 4;
+  constexpr int kFirstTiles = kStages / 2;            // tiles the start-up loads touch
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot[kPhaseBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vslot[kPhaseBytes];
   __shared__ int blk_ids[kMaxChunkTiles];
-  __shared__ float half_ml[4][16][2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hg = wave & 3;     // head group
-  const int kh = wave >> 2;    // key half
-  const int r = lane & 15;     // MFMA row / column index of this lane
-  const int q4 = lane >> 4;    // K-group of this lane
+  const bool loader = wave >= 4;
   const int bg = blockIdx.y;
   const int b = bg / p.hkv;
   const int g = bg - b * p.hkv;
   const int split = blockIdx.x;
-  const int head = g * kG + hg * 16 + r;    // this lane's query head
-  const float qk_scale = p.scale * kLog2e * (kFp8 ? p.k_scale[g] : 1.f);
   const int32_t* trow = p.block_table ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
 
   // Dense attention: the split's first page (split * chunk) does not depend
-  // on the slot length, so its block id is fetched together with the length
-  // and its K/V loads are in flight before the length is known (a split that
-  // turns out to be past the end simply drops them).  With a window the
-  // first page moves with the length.
+  // on the slot length, so its block ids are fetched together with the
+  // length and the loaders' first K/V loads are in flight before the length
+  // is known (a split that turns out to be past the end simply drops them).
+  // With a window the first page moves with the length.
   int t_begin = kDense ? min(split * p.chunk_tiles, p.max_blocks - 1) : 0;
   int blk_first[kFirstTiles];
 #pragma unroll
   for (int i = 0; i < kFirstTiles; ++i)
-    blk_first[i] = (kDense && trow) ? trow[min(t_begin + i, p.max_blocks - 1)] : 0;
+    blk_first[i] = (kDense && trow && loader) ? trow[min(t_begin + i, p.max_blocks - 1)] : 0;
   const int L = slot_len(p.ctx_lens[b], p.max_blocks);
   int nphase = 0;   // two phases (K, V) per tile of this split; set once L is known
 
+  // ---- loader state ----
+  // Loader thread lt copies 16-byte chunks idx = lt + 256 k of a phase.
+  //  bf16: rows (lt >> 5) + 8k of a K tile (32 chunks per row), rows
+  //        (lt >> 3) + 32k of a V^T tile (8 chunks per row).
+  //  FP8:  rows (lt >> 4) + 16k of a K tile (16 code chunks per row) and
+  //        rows (lt >> 2) + 64k of a V^T tile (4 per row); code chunk c
+  //        becomes bf16 chunks 2c and 2c + 1 of the same LDS row.
+  const int lt = tid & (kLoaders - 1);
   const char* kpool = static_cast<const char*>(p.k);
   const char* vpool = static_cast<const char*>(p.v);
-  // This thread's 16-byte chunks of a phase, idx = tid + 512 k.
-  //  bf16: rows (tid >> 5) + 16k of a K tile (32 chunks per row), rows
-  //        (tid >> 3) + 64k of a V^T tile (8 chunks per row).  The V^T
-  //        swizzle repeats every 16 rows, the K swizzle every 32: odd k flip
-  //        bit 3 of the K chunk index.
-  //  FP8:  rows (tid >> 4) + 32k of a K tile (16 code chunks per row) and
-  //        rows (tid >> 2) + 128k of a V^T tile (4 per row); code chunk c
-  //        becomes bf16 chunks 2c and 2c + 1 of the same LDS row, and the
-  //        row steps keep the swizzle.
-  const int krow0 = kFp8 ? tid >> 4 : tid >> 5, kc = kFp8 ? tid & 15 : tid & 31;
-  const int vrow0 = kFp8 ? tid >> 2 : tid >> 3, vc = kFp8 ? tid & 3 : tid & 7;
+  const int krow0 = kFp8 ? lt >> 4 : lt >> 5, kc = kFp8 ? lt & 15 : lt & 31;
+  const int vrow0 = kFp8 ? lt >> 2 : lt >> 3, vc = kFp8 ? lt & 3 : lt & 7;
   const int64_t kgoff0 = ((int64_t)krow0 * p.k_row_stride + kc * (16 / kElem)) * kElem;
   const int64_t vgoff0 = ((int64_t)vrow0 * p.v_row_stride + vc * (16 / kElem)) * kElem;
-  const int64_t kgstep = (int64_t)(kFp8 ? 32 : 16) * p.k_row_stride * kElem;
-  const int64_t vgstep = (int64_t)(kFp8 ? 128 : 64) * p.v_row_stride * kElem;
-  const uint32_t klds_even = krow0 * 512 + ((kc ^ swz_k(krow0)) << 4);
-  const uint32_t klds_odd = krow0 * 512 + ((kc ^ swz_k(krow0 + 16)) << 4);
-  const uint32_t vlds0 = vrow0 * 128 + ((vc ^ swz_v(vrow0)) << 4);
-  const uint32_t k8_lo = krow0 * 512 + (((2 * kc) ^ swz_k(krow0)) << 4);
-  const uint32_t k8_hi = krow0 * 512 + (((2 * kc + 1) ^ swz_k(krow0)) << 4);
-  const uint32_t v8_lo = vrow0 * 128 + (((2 * vc) ^ swz_v(vrow0)) << 4);
-  const uint32_t v8_hi = vrow0 * 128 + (((2 * vc + 1) ^ swz_v(vrow0)) << 4);
+  const int64_t kgstep = (int64_t)(kFp8 ? 16 : 8) * p.k_row_stride * kElem;
+  const int64_t vgstep = (int64_t)(kFp8 ? 64 : 32) * p.v_row_stride * kElem;
+  // LDS position of bf16 chunk c of K row krow0 + (8 or 16) k.
+  auto klds = [&](int k, int c) {
+    const int row = krow0 + (kFp8 ? 16 : 8) * k;
+    return (uint32_t)(row * 512 + ((c ^ swz_k(row)) << 4));
+  };
+  const int xv_st = swz_v(vrow0);   // V^T rows step by 32 or 64: same swizzle
 
-  // Register-staged loads of one phase (nothing past the end of the split).
-  // The first two phases take their block ids straight from the table, so
-  // they are in flight before the id cache in LDS is filled.
+  // Register-staged loads of one phase (tiles clamped into the table row:
+  // the start-up loads may run past the split).
   auto load_phase = [&](int ph, intx4* st, int blk) {
-    const int tile = min(t_begin + (ph >> 1), p.max_blocks - 1);   // start-up loads run ahead
+    const int tile = min(t_begin + (ph >> 1), p.max_blocks - 1);
     if ((ph & 1) == 0) {
       const char* base =
           kpool + ((p.block_table ? (int64_t)blk : (int64_t)b * p.max_blocks + tile) * p.k_block_stride +
@@ -177,67 +191,52 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   // cache rows may hold anything, NaN included), so the PV product never
   // multiplies garbage by a zero probability.  A bf16 chunk holds 8
   // consecutive keys of one channel (vc*8 .. vc*8+7; FP8: 16 keys vc*16 ..).
-  auto keep_mask = [&](int valid, uint32_t* keep) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      keep[e] = ((2 * e < valid) ? 0x0000ffffu : 0u) | ((2 * e + 1 < valid) ? 0xffff0000u : 0u);
-  };
-  auto apply = [](intx4 v, const uint32_t* keep) {
-    v.x &= keep[0];
-    v.y &= keep[1];
-    v.z &= keep[2];
-    v.w &= keep[3];
-    return v;
-  };
   auto store_phase = [&](int ph, const intx4* st) {
     if (ph >= nphase) return;
-    uint8_t* dst = ring + (ph % kRing) * kPhaseBytes;
     const int key_rel = L - (t_begin + (ph >> 1)) * kPage;   // keys of this tile < L
-    if (kFp8) {
-      if (ph & 1) {
-        uint32_t keep_lo[4], keep_hi[4];
-        keep_mask(key_rel - vc * 16, keep_lo);
-        keep_mask(key_rel - vc * 16 - 8, keep_hi);
+    if ((ph & 1) == 0) {
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
+      for (int k = 0; k < kPerThread; ++k) {
+        if (kFp8) {
           intx4 lo, hi;
           e4m3x16_to_bf16(st[k], lo, hi);
-          *reinterpret_cast<intx4*>(dst + v8_lo + k * 128 * 128) = apply(lo, keep_lo);
-          *reinterpret_cast<intx4*>(dst + v8_hi + k * 128 * 128) = apply(hi, keep_hi);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-          intx4 lo, hi;
-          e4m3x16_to_bf16(st[k], lo, hi);
-          *reinterpret_cast<intx4*>(dst + k8_lo + k * 32 * 512) = lo;
-          *reinterpret_cast<intx4*>(dst + k8_hi + k * 32 * 512) = hi;
+          *reinterpret_cast<intx4*>(kslot + klds(k, 2 * kc)) = lo;
+          *reinterpret_cast<intx4*>(kslot + klds(k, 2 * kc + 1)) = hi;
+        } else {
+          *reinterpret_cast<intx4*>(kslot + klds(k, kc)) = st[k];
         }
       }
-    } else if (ph & 1) {
+    } else if (kFp8) {
+      uint32_t keep_lo[4], keep_hi[4];
+      keep_mask(key_rel - vc * 16, keep_lo);
+      keep_mask(key_rel - vc * 16 - 8, keep_hi);
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        intx4 lo, hi;
+        e4m3x16_to_bf16(st[k], lo, hi);
+        const int row = vrow0 + 64 * k;
+        *reinterpret_cast<intx4*>(vslot + row * 128 + (((2 * vc) ^ xv_st) << 4)) = apply_keep(lo, keep_lo);
+        *reinterpret_cast<intx4*>(vslot + row * 128 + (((2 * vc + 1) ^ xv_st) << 4)) = apply_keep(hi, keep_hi);
+      }
+    } else {
       uint32_t keep[4];
       keep_mask(key_rel - vc * 8, keep);
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k)
-        *reinterpret_cast<intx4*>(dst + vlds0 + k * 64 * 128) = apply(st[k], keep);
-    } else {
-#pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
-        const uint32_t base_off = (k & 1) ? klds_odd : klds_even;
-        *reinterpret_cast<intx4*>(dst + base_off + k * 16 * 512) = st[k];
+        const int row = vrow0 + 32 * k;
+        *reinterpret_cast<intx4*>(vslot + row * 128 + ((vc ^ xv_st) << 4)) = apply_keep(st[k], keep);
       }
     }
   };
 
   intx4 stage[kStages][kPerThread];
-  // The first kStages phases, block ids straight from the table (tiles past
-  // the split's end are clamped into the table row and never published).
+  // The first kStages phases, block ids straight from the table.
   auto load_first = [&]() {
 #pragma unroll
     for (int ph = 0; ph < kStages; ++ph)
       load_phase(ph, stage[ph], pool_block(readfirstlane(blk_first[ph >> 1]), p.num_blocks));
   };
-  if (kDense) load_first();
+  if (kDense && loader) load_first();
 
   const int lo = (!kDense && L > p.window) ? L - p.window : 0;
   int n_tiles = 0, t_lo = 0;
@@ -248,102 +247,171 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   if (!kDense) t_begin = t_lo + split * p.chunk_tiles;
   const int t_end = min(t_lo + n_tiles, t_begin + p.chunk_tiles);
 
+  // ---- compute-wave identity ----
+  const int hg = wave & 3;     // head group: heads 16hg .. 16hg+15 of the KV group
+  const int r = lane & 15;     // MFMA row / column of this lane
+  const int q4 = lane >> 4;    // K-group of this lane
+  const int head = g * kG + hg * 16 + r;    // this lane's query head
+
   if (t_begin >= t_end || (kDense && split * p.chunk_tiles >= p.max_blocks)) {
-    if (kh == 0) {
-      if (p.splits == 1) {   // empty slot: zeros
-        for (int ct = 0; ct < kD / 16; ++ct) {
-          const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
-          if (p.out_f32)
-            *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
-          else
-            *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
-        }
-      } else if (q4 == 0) {  // no keys in this split: an empty partial for the merge
-        const int64_t row = ((int64_t)bg * p.splits + split) * kG + hg * 16 + r;
-        *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{kNegInf, 0.f};
+    if (loader) return;
+    if (p.splits == 1) {   // empty slot: zeros
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
+        if (p.out_f32)
+          *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
+        else
+          *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
       }
+    } else if (q4 == 0) {  // no keys in this split: an empty partial for the merge
+      const int64_t row = ((int64_t)bg * p.splits + split) * kG + hg * 16 + r;
+      *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{kNegInf, 0.f};
     }
     return;
   }
   const int nt = t_end - t_begin;
   nphase = 2 * nt;
 
-  // Start-up order: the first kStages phases are in flight (dense) or go
-  // first, then the block-id cache (rows t_begin .. t_end-1 of the table),
-  // then Q; only LDS is fenced before the loop.  (Loads are issued
-  // unconditionally, indices clamped: the compiler's wait counts stay exact
-  // only when every path issues the same loads.)
-  if (!kDense) {
+  // Start-up: the loaders' first kStages phases are in flight (dense) or go
+  // first; every thread fills part of the block-id cache (rows t_begin ..
+  // t_end-1 of the table); the compute waves load Q; the loaders publish
+  // phase 0.  (Loads are issued unconditionally, indices clamped: the
+  // compiler's wait counts stay exact only when every path issues the same
+  // loads.)
+  if (!kDense && loader) {
 #pragma unroll
     for (int i = 0; i < kFirstTiles; ++i)
       blk_first[i] = trow ? trow[min(t_begin + i, p.max_blocks - 1)] : 0;
     load_first();
   }
+  constexpr int kIdsPerThread = kMaxChunkTiles / kThreads;
   const int32_t* btab = trow ? trow + t_begin : static_cast<const int32_t*>(p.ctx_lens);
-  int blk_cache[(kMaxChunkTiles + kThreads - 1) / kThreads];
+  int blk_cache[kIdsPerThread];
 #pragma unroll
-  for (int k = 0; k < (kMaxChunkTiles + kThreads - 1) / kThreads; ++k)
+  for (int k = 0; k < kIdsPerThread; ++k)
     blk_cache[k] = btab[trow ? min(tid + k * kThreads, nt - 1) : 0];
-  // Q fragments (B operand of S^T): this lane's head, channels 32s + 8q4 .. +7.
+#pragma unroll
+  for (int k = 0; k < kIdsPerThread; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < nt) blk_ids[i] = pool_block(blk_cache[k], p.num_blocks);
+  }
+
+  if (loader) {
+    store_phase(0, stage[0]);
+    lds_barrier();   // block ids and phase 0 visible
+    // Phase kStages into the freed stage (clamped to the last tile, same K/V
+    // parity, when the split is shorter; such a copy is never published).
+    load_phase_cached(min(kStages, nphase - 2), stage[0]);
+    // Step q: barrier q, publish phase q+1 (loaded kStages steps ago) into
+    // its slot, load phase q+1+kStages into the registers it freed.  Phase
+    // i lives in stage i % kStages; steps are unrolled kStages at a time.
+    auto step = [&](auto ic, int q, bool more) {
+      constexpr int I = decltype(ic)::value;     // q % kStages
+      constexpr int st = (I + 1) % kStages;
+      lds_barrier();
+      store_phase(q + 1, stage[st]);
+      if (more) load_phase_cached(q + 1 + kStages, stage[st]);
+    };
+    auto group = [&](int q, auto all_in_range) {
+      auto one = [&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        if constexpr (decltype(all_in_range)::value) {
+          step(ic, q + I, true);
+        } else {
+          if (q + I < nphase) step(ic, q + I, q + I + 1 + kStages < nphase);
+        }
+      };
+      one(Int<0>{});
+      one(Int<1>{});
+      one(Int<2>{});
+      one(Int<3>{});
+      if constexpr (kStages == 8) {
+        one(Int<4>{});
+        one(Int<5>{});
+        one(Int<6>{});
+        one(Int<7>{});
+      }
+    };
+    // Main loop: every load it issues is in range, so the issue pattern (and
+    // the compiler's wait counts) is the same in every iteration.
+    int q = 0;
+    for (; q + 2 * kStages < nphase; q += kStages) group(q, std::true_type{});
+    for (; q < nphase; q += kStages) group(q, std::false_type{});
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const float qk_scale = p.scale * kLog2e * (kFp8 ? p.k_scale[g] : 1.f);
+  // Q fragments (B operand of S^T): this lane's head, channels 32c + 8q4 .. +7.
   intx4 qf[kD / 32];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD + q4 * 8;
 #pragma unroll
-    for (int s = 0; s < kD / 32; ++s) qf[s] = *reinterpret_cast<const intx4*>(qp + s * 32);
+    for (int c = 0; c < kD / 32; ++c) qf[c] = *reinterpret_cast<const intx4*>(qp + c * 32);
   }
-#pragma unroll
-  for (int k = 0; k < (kMaxChunkTiles + kThreads - 1) / kThreads; ++k) {
-    const int i = tid + k * kThreads;
-    if (i < nt) blk_ids[i] = pool_block(blk_cache[k], p.num_blocks);
-  }
-  store_phase(0, stage[0]);
   lds_barrier();   // block ids and phase 0 visible
-  // Phase kStages into the freed stage (clamped to the last tile, same K/V
-  // parity, when the split is shorter; such a copy is never published).
-  load_phase_cached(min(kStages, nphase - 2 + (kStages & 1)), stage[0]);
 
-  // K operand row of S^T tile j: key = 32kh + 8(r/4) + 4j + r%4; its swizzle
-  // does not depend on j (bit 2 of the key is not used).
-  const int key_lane = 32 * kh + 8 * (r >> 2) + (r & 3);
-  const int xk = swz_k(key_lane);
-  const int xv = swz_v(r);
+  // K operand of S^T tile j: row r is key 32(j/2) + 8(r/4) + 4(j%2) + r%4,
+  // whose swizzle is r itself; fragment c (channels 32c + 8q4 .. +7) is
+  // chunk (4c + q4) ^ r = 4c ^ (q4 ^ r), at byte (kfrag ^ (c << 6)) +
+  // 512 (32(j/2) + 4(j%2)).
+  const uint32_t kfrag = (8 * (r >> 2) + (r & 3)) * 512 + ((q4 ^ r) << 4);
+  // V^T operand of channel tile t, key step s: row 16t + r, chunk
+  // (4s + q4) ^ swz_v(r), at byte vfrag_s + 2048 t.
+  const uint32_t vfrag0 = r * 128 + ((q4 ^ swz_v(r)) << 4);
+  const uint32_t vfrag1 = r * 128 + (((4 + q4) ^ swz_v(r)) << 4);
 
   float m_run = kNegInf;
   float l_run = 0.f;
   floatx4 acc[kD / 16];
 #pragma unroll
   for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-  intx4 pb;
+  intx4 pb[2];
 
-  auto k_phase = [&](const uint8_t* buf, int key0) {
-    floatx4 st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  auto k_phase = [&](int key0) {
+    uint32_t kb = kfrag;
+    asm volatile("" : "+v"(kb));   // addresses formed here, not hoisted and kept live
+    floatx4 st[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    intx4 a[kD / 32][4];
 #pragma unroll
-    for (int s = 0; s < kD / 32; ++s) {
-      const int chunk = (4 * s + q4) ^ xk;
+    for (int c = 0; c < kD / 32; ++c) {
+      const uint32_t a_off = kb ^ (c << 6);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const intx4 a = *reinterpret_cast<const intx4*>(buf + (key_lane + 4 * j) * 512 + chunk * 16);
-        st[j] = mfma_bf16_16x16x32(a, qf[s], st[j]);
-      }
+      for (int j = 0; j < 4; ++j)
+        a[c][j] = *reinterpret_cast<const intx4*>(kslot + a_off + ((j >> 1) * 32 + (j & 1) * 4) * 512);
     }
-    // This lane's keys are key0 + 32kh + 8q4 + e, e = 4j + i; those in
-    // [lo, L) are attended.  Interior tiles have e_lo <= 0 and e_hi >= 8.
-    const int ebase = key0 + 32 * kh + 8 * q4;
-    const int e_lo = lo - ebase, e_hi = L - ebase;
-    float sv[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int c = 0; c < kD / 32; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st[j] = mfma_bf16_16x16x32(a[c][j], qf[c], st[j]);
+    // Software pipeline: operands of eight products in flight ahead of the
+    // matrix unit (the other wave on this SIMD is a loader).
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    // Lane values: tile j, element i is key key0 + 32(j/2) + 8q4 + 4(j%2) + i;
+    // those in [lo, L) are attended.
+    const int ebase = key0 + 8 * q4;
+    const int e_lo = lo - ebase, e_hi = L - ebase;
+    float sv[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = 4 * j + i;
+        const int e = 32 * (j >> 1) + 4 * (j & 1) + i;
         const float x = st[j][i] * qk_scale;
         sv[j][i] = (e >= e_lo && e < e_hi) ? x : kNegInf;
       }
-    float mx = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      mx = fmaxf(mx, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
     mx = wave_max_xor16_32(mx);
     // Lazy max: keep the old reference unless this tile exceeds it by > 2^8.
-    // (A half-tile can be fully masked: mx = -inf and nothing moves.)
     const bool move = mx > m_run + kLazyRescale;
     const float m_new = move ? mx : m_run;
     if (__any(move && m_run != kNegInf)) {
@@ -355,101 +423,51 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sv[j][i] = m_new == kNegInf ? 0.f : fast_exp2(sv[j][i] - m_new);
         psum += sv[j][i];
       }
     l_run += psum;
-    // P^T B operand (keys 8q4 .. 8q4+7 of the half).
-    pb = intx4{(int)pack_bf16x2(sv[0][0], sv[0][1]), (int)pack_bf16x2(sv[0][2], sv[0][3]),
-               (int)pack_bf16x2(sv[1][0], sv[1][1]), (int)pack_bf16x2(sv[1][2], sv[1][3])};
+    // P^T B operands: keys 32s + 8q4 .. +7 come from tiles 2s (first four)
+    // and 2s + 1 (last four).
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      pb[s] = intx4{(int)pack_bf16x2(sv[2 * s][0], sv[2 * s][1]), (int)pack_bf16x2(sv[2 * s][2], sv[2 * s][3]),
+                    (int)pack_bf16x2(sv[2 * s + 1][0], sv[2 * s + 1][1]),
+                    (int)pack_bf16x2(sv[2 * s + 1][2], sv[2 * s + 1][3])};
   };
 
-  auto v_phase = [&](const uint8_t* buf) {
-    const int chunk = (4 * kh + q4) ^ xv;
+  auto v_phase = [&]() {
+    intx4 a[2][kD / 16];
 #pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      const intx4 a = *reinterpret_cast<const intx4*>(buf + ct * 2048 + r * 128 + chunk * 16);
-      acc[ct] = mfma_bf16_16x16x32(a, pb, acc[ct]);
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct)
+        a[s][ct] = *reinterpret_cast<const intx4*>(vslot + (s ? vfrag1 : vfrag0) + ct * 2048);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = mfma_bf16_16x16x32(a[s][ct], pb[s], acc[ct]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
-  // Step ph: publish phase ph+1 (loaded kStages steps ago) into its slot,
-  // start loading phase ph+1+kStages into the freed registers, barrier,
-  // compute phase ph.  Slot ph+1 last held phase ph-2, finished by every wave
-  // before the barrier of step ph-1.  Phase q lives in stage q % kStages;
-  // steps are unrolled kUnroll at a time (a multiple of kStages and of the
-  // K/V period), so every stage index is a constant.
-  auto step = [&](auto ic, int ph, bool more) {
-    constexpr int I = decltype(ic)::value;        // ph % kUnroll
-    constexpr int st = (I + 1) % kStages;
-    store_phase(ph + 1, stage[st]);
-    if (more) load_phase_cached(ph + 1 + kStages, stage[st]);
-    lds_barrier();
-    if ((I & 1) == 0)
-      k_phase(ring + (ph % kRing) * kPhaseBytes, (t_begin + (ph >> 1)) * kPage);
-    else
-      v_phase(ring + (ph % kRing) * kPhaseBytes);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  using I5 = std::integral_constant<int, 5>;
-  // Main loop: every load it issues is in range, so the issue pattern (and
-  // the compiler's wait counts) is the same in every iteration.
-  int ph = 0;
-  for (; ph + kUnroll + kStages < nphase; ph += kUnroll) {
-    step(I0{}, ph, true);
-    step(I1{}, ph + 1, true);
-    step(I2{}, ph + 2, true);
-    step(I3{}, ph + 3, true);
-    if constexpr (kUnroll == 6) {
-      step(I4{}, ph + 4, true);
-      step(I5{}, ph + 5, true);
-    }
-  }
-  // Tail: the last tiles (loads only while in range).
-  for (; ph < nphase; ph += kUnroll) {
-    step(I0{}, ph, ph + 1 + kStages < nphase);
-    step(I1{}, ph + 1, ph + 2 + kStages < nphase);
-    if (ph + 2 >= nphase) break;
-    step(I2{}, ph + 2, ph + 3 + kStages < nphase);
-    step(I3{}, ph + 3, ph + 4 + kStages < nphase);
-    if constexpr (kUnroll == 6) {
-      if (ph + 4 >= nphase) break;
-      step(I4{}, ph + 4, ph + 5 + kStages < nphase);
-      step(I5{}, ph + 5, ph + 6 + kStages < nphase);
-    }
+  for (int t = 0; t < nt; ++t) {
+    lds_barrier();   // K tile t visible
+    k_phase((t_begin + t) * kPage);
+    lds_barrier();   // V^T tile t visible
+    v_phase();
   }
 
-  // ---- merge the two key halves of each head group ----
-  lds_barrier();   // every wave is done with the ring
-  const float l_half = wave_sum_xor16_32(l_run);
-  float* obuf = reinterpret_cast<float*>(ring);   // [4 head groups][16 heads][256]
-  if (kh == 1) {
-    if (q4 == 0) {
-      half_ml[hg][r][0] = m_run;
-      half_ml[hg][r][1] = l_half;
-    }
-#pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct)
-      *reinterpret_cast<floatx4*>(obuf + (hg * 16 + r) * kD + ct * 16 + q4 * 4) = acc[ct];
-  }
-  lds_barrier();
-  if (kh == 1) return;
-  const float m1 = half_ml[hg][r][0], l1 = half_ml[hg][r][1];
-  const float M = fmaxf(m_run, m1);
-  const float w0 = m_run == kNegInf ? 0.f : fast_exp2(m_run - M);
-  const float w1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - M);
-  const float l_tot = w0 * l_half + w1 * l1;
-#pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct)
-    acc[ct] = w0 * acc[ct] + w1 * *reinterpret_cast<const floatx4*>(obuf + (hg * 16 + r) * kD + ct * 16 + q4 * 4);
-
+  // ---- finish: this wave holds every key of its 16 heads ----
+  const float l_tot = wave_sum_xor16_32(l_run);
   if (p.splits == 1) {
     const float inv = (kFp8 ? p.v_scale[g] : 1.f) / l_tot;
 #pragma unroll
@@ -467,7 +485,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int ct = 0; ct < kD / 16; ++ct)
       *reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4) = acc[ct];
-    if (q4 == 0) *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{M, l_tot};
+    if (q4 == 0) *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{m_run, l_tot};
   }
 }
 
