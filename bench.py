@@ -145,6 +145,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph instead of launching it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -199,24 +201,41 @@ def main():
                                          v_scale=t["v_scale"], num_splits=args.num_splits)
 
     log(f"bench: warmup {args.warmup}")
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, len(pools))):
         call(i)
     torch.cuda.synchronize()
+    step = call
+    if args.graph:
+        # The same launches replayed from captured graphs (one per pool copy).
+        graphs = []
+        for i in range(len(pools)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+        def step(i):
+            graphs[i % len(graphs)].replay()
+    # One HIP event pair brackets the K timed steps on the launch stream (an
+    # event pair around every call would add its own marker packets, several
+    # microseconds each, between the kernels it measures).
     stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    start.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
-        call(i)
-        ends[i].record(stream)
+        step(i)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1e3 / args.steps
-    call_ms = float(np.mean(per_call_ms))
+    call_ms = start.elapsed_time(end) / args.steps
 
     fmt_kv = case.kv_format
     nbytes = accounting.decode_call_bytes(case.ctx_lens, hq=case.hq, hkv=case.hkv, d=case.d,
@@ -244,18 +263,18 @@ def main():
         "config": {"workload": WORKLOADS[args.config], "batch": case.batch,
                    "ctx_len_mean": float(np.mean(case.ctx_lens)), "q_heads": case.hq,
                    "kv_heads": case.hkv, "head_dim": case.d, "kv_dtype": fmt_kv,
-                   "page": 64, "window": window, "splits": splits, "kv_pool_copies": len(pools)},
+                   "page": 64, "window": window, "splits": splits, "kv_pool_copies": len(pools),
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "hbm_gbps": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "call_us_mean": call_ms * 1e3,
-        "call_us_p10_p90": [float(np.percentile(per_call_ms, 10) * 1e3),
-                            float(np.percentile(per_call_ms, 90) * 1e3)],
         "algorithmic_bytes_per_call": nbytes,
         "flops_per_call": flops,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(args.config),
-                     "timed": "HIP events around each call (attention kernel + split merge "
-                              "kernel) on the launch stream"},
+                     "timed": "one HIP event pair around the timed steps on the launch "
+                              "stream, divided by the step count (attention kernel + split "
+                              "merge kernel per step)"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample of the same workload")

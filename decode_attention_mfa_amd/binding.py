@@ -81,13 +81,29 @@ def mfa_decode_plan_splits(desc, window=0, num_cus=256):
     return int(_lib.load().mfa_decode_plan_splits(ctypes.byref(desc), int(window), int(num_cus)))
 
 
+# Descriptor and workspace size per call shape: a decode loop calls with the
+# same shapes every step, so the marshalling cost is paid once.
+_plans = {}
+
+
+def _plan(q, k_cache, block_table, out, num_splits, window):
+    key = (tuple(q.shape), q.dtype, tuple(k_cache.shape), k_cache.dtype,
+           None if block_table is None else tuple(block_table.shape), out.dtype,
+           int(num_splits), int(window), q.device.index)
+    plan = _plans.get(key)
+    if plan is None:
+        desc = decode_desc(q, k_cache, block_table, out, num_splits)
+        plan = (desc, ctypes.byref(desc), mfa_decode_workspace_size(desc, window))
+        _plans[key] = plan
+    return plan
+
+
 def _decode(entry, q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_scale, v_scale,
             window, num_splits, workspace, stream):
     lib = _lib.load()
-    desc = decode_desc(q, k_cache, block_table, out, num_splits)
-    need = mfa_decode_workspace_size(desc, window)
+    _, desc_ref, need = _plan(q, k_cache, block_table, out, num_splits, window)
     ws, ws_bytes = _workspace(q.device, need, workspace, "decode")
-    args = [ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+    args = [desc_ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
             _ptr(ctx_lens), _ptr(k_scale), _ptr(v_scale), _ptr(out), ctypes.c_float(scale)]
     if entry == "gqa":
         args.append(ctypes.c_int32(int(window)))

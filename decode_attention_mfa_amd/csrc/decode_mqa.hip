@@ -30,6 +30,13 @@
 // reduced once at the end; a compute wave holds all keys of its heads, so
 // its output (or split partial) is final without any merge between waves.
 //
+// FP8 E4M3 caches stay 8-bit in LDS (K rows of 256 B, V^T rows of 64 B) and
+// are widened to bf16 in registers after the read.  The MFMA k-index <->
+// channel and row <-> key maps are chosen so that one 16-byte LDS read of a
+// lane holds the operands of two products: QK^T step c takes channels
+// 64(c/2) + 16(l/16) + 8(c%2) + e, S^T row r of tile j is key
+// 16(r/4) + 4j + r%4, and PV step s takes keys 16(l/16) + 8s + e.
+//
 // Online softmax in the log2 domain, fp32 state.  The running max only moves
 // when a tile's max exceeds it by more than kLazyRescale (2^8 headroom for
 // p = 2^(s - m) in fp32/bf16), so O is rescaled a handful of times per split;
@@ -56,6 +63,12 @@ constexpr float kLazyRescale = 8.f;    // log2 headroom before the max moves
 // channels (two per 256-byte bank row).
 __device__ __forceinline__ int swz_k(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
 __device__ __forceinline__ int swz_v(int ch) { return (ch & 7) ^ ((ch >> 3) & 1); }
+// FP8 tiles (16-byte chunks of 16 codes): the 16 lanes of one K read hold
+// keys {0..3, 16..19, 32..35, 48..51} + const (rows of 256 B, one bank row
+// each); the 16 lanes of one V^T read hold 16 consecutive channels (rows of
+// 64 B, four per bank row).
+__device__ __forceinline__ int swz_k8(int key) { return (key & 3) | (((key >> 4) & 3) << 2); }
+__device__ __forceinline__ int swz_v8(int ch) { return (ch >> 2) & 3; }
 
 // Workgroup barrier ordering LDS only: release/acquire fences scoped to the
 // workgroup and to the local (LDS) address space, around s_barrier.  The
@@ -68,18 +81,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Converts 16 E4M3 codes (one 16-byte chunk) to two 16-byte bf16 chunks.
-// Every E4M3FN value is a bf16 value, and the conversion scale is 1, so this
-// is exact (NaN codes stay NaN).
+// Eight E4M3 codes (two dwords, codes in byte order) to the eight bf16 of
+// an MFMA operand.  Every E4M3FN value is a bf16 value and the conversion
+// scale is 1, so this is exact (NaN codes stay NaN).
 template <bool kUpper>
 __device__ __forceinline__ int e4m3x2_to_bf16x2(int w) {   // codes of bytes 0,1 (or 2,3)
   return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kUpper));
 }
-__device__ __forceinline__ void e4m3x16_to_bf16(intx4 raw, intx4& lo, intx4& hi) {
-  lo = intx4{e4m3x2_to_bf16x2<false>(raw.x), e4m3x2_to_bf16x2<true>(raw.x),
-             e4m3x2_to_bf16x2<false>(raw.y), e4m3x2_to_bf16x2<true>(raw.y)};
-  hi = intx4{e4m3x2_to_bf16x2<false>(raw.z), e4m3x2_to_bf16x2<true>(raw.z),
-             e4m3x2_to_bf16x2<false>(raw.w), e4m3x2_to_bf16x2<true>(raw.w)};
+__device__ __forceinline__ intx4 e4m3x8_to_bf16(int w0, int w1) {
+  return intx4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+               e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)};
 }
 
 // Keep masks for a bf16 chunk of 8 consecutive keys of which `valid` (may be
@@ -88,6 +99,16 @@ __device__ __forceinline__ void keep_mask(int valid, uint32_t* keep) {
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     keep[e] = ((2 * e < valid) ? 0x0000ffffu : 0u) | ((2 * e + 1 < valid) ? 0xffff0000u : 0u);
+}
+// The same for a chunk of 16 consecutive E4M3 keys (one byte each).
+__device__ __forceinline__ void keep_mask8(int valid, uint32_t* keep) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m |= (4 * e + i < valid) ? (0xffu << (8 * i)) : 0u;
+    keep[e] = m;
+  }
 }
 __device__ __forceinline__ intx4 apply_keep(intx4 v, const uint32_t* keep) {
   v.x &= keep[0];
@@ -100,20 +121,25 @@ __device__ __forceinline__ intx4 apply_keep(intx4 v, const uint32_t* keep) {
 template <int N>
 using Int = std::integral_constant<int, N>;
 
-// kDense: no window (the split's first page is known before the length).
-// kFp8: the cache holds OCP E4M3 codes with one fp32 scale per KV head; tiles
-// are converted to bf16 as they are written to LDS, and the scales are
-// applied to the logits (k) and to the normalised output (v).
-template <bool kDense, bool kFp8>
+// kK8 / kV8 (FP8 only): K / V^T tiles stay E4M3 codes in LDS and the
+// compute waves widen their operands; otherwise the loaders widen the codes
+// to bf16 as they publish a phase.  8-bit K tiles use the key <-> row map
+// that lets one 16-byte read feed two products (see above).
+template <bool kDense, bool kFp8, bool kK8, bool kV8>
 __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
+  static_assert(kFp8 || (!kK8 && !kV8), "8-bit LDS tiles need an FP8 cache");
+  static_assert(kK8 || !kV8, "8-bit V^T tiles use the 8-bit K key map");
+  constexpr bool kMap16 = kK8;                          // key map of 8-bit K tiles
   constexpr int kElem = kFp8 ? 1 : 2;                 // bytes per cached element
   constexpr int kPerThread = kPhaseBytes * kElem / 2 / 16 / kLoaders;   // 16-byte loads per phase
+  constexpr int kKSlot = kK8 ? kPhaseBytes / 2 : kPhaseBytes;   // LDS bytes of a K tile
+  constexpr int kVSlot = kV8 ? kPhaseBytes / 2 : kPhaseBytes;   // and of a V^T tile
   // Phases in flight in the loaders' registers: 4 bf16 or 8 FP8 phases,
   // 128 KB of cache data per CU either way.
   constexpr int kStages = kFp8 ? 8 : 4;
   constexpr int kFirstTiles = kStages / 2;            // tiles the start-up loads touch
-  __shared__ __attribute__((aligned(1024))) uint8_t kslot[kPhaseBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t vslot[kPhaseBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot[kKSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t vslot[kVSlot];
   __shared__ int blk_ids[kMaxChunkTiles];
 
   const int tid = threadIdx.x;
@@ -144,8 +170,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   //  bf16: rows (lt >> 5) + 8k of a K tile (32 chunks per row), rows
   //        (lt >> 3) + 32k of a V^T tile (8 chunks per row).
   //  FP8:  rows (lt >> 4) + 16k of a K tile (16 code chunks per row) and
-  //        rows (lt >> 2) + 64k of a V^T tile (4 per row); code chunk c
-  //        becomes bf16 chunks 2c and 2c + 1 of the same LDS row.
+  //        rows (lt >> 2) + 64k of a V^T tile (4 per row), copied as codes.
   const int lt = tid & (kLoaders - 1);
   const char* kpool = static_cast<const char*>(p.k);
   const char* vpool = static_cast<const char*>(p.v);
@@ -155,12 +180,19 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   const int64_t vgoff0 = ((int64_t)vrow0 * p.v_row_stride + vc * (16 / kElem)) * kElem;
   const int64_t kgstep = (int64_t)(kFp8 ? 16 : 8) * p.k_row_stride * kElem;
   const int64_t vgstep = (int64_t)(kFp8 ? 64 : 32) * p.v_row_stride * kElem;
-  // LDS position of bf16 chunk c of K row krow0 + (8 or 16) k.
+  // LDS position of stored chunk c (16 codes or 8 bf16) of K row
+  // krow0 + (8 or 16) k.
   auto klds = [&](int k, int c) {
     const int row = krow0 + (kFp8 ? 16 : 8) * k;
-    return (uint32_t)(row * 512 + ((c ^ swz_k(row)) << 4));
+    return kK8 ? (uint32_t)(row * 256 + ((c ^ swz_k8(row)) << 4))
+               : (uint32_t)(row * 512 + ((c ^ swz_k(row)) << 4));
   };
-  const int xv_st = swz_v(vrow0);   // V^T rows step by 32 or 64: same swizzle
+  // V^T rows step by 32 or 64: the swizzle of the first row holds for all.
+  auto vlds = [&](int k, int c) {
+    const int row = vrow0 + (kFp8 ? 64 : 32) * k;
+    return kV8 ? (uint32_t)(row * 64 + ((c ^ swz_v8(vrow0)) << 4))
+               : (uint32_t)(row * 128 + ((c ^ swz_v(vrow0)) << 4));
+  };
 
   // Register-staged loads of one phase (tiles clamped into the table row:
   // the start-up loads may run past the split).
@@ -197,35 +229,32 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     if ((ph & 1) == 0) {
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
-        if (kFp8) {
-          intx4 lo, hi;
-          e4m3x16_to_bf16(st[k], lo, hi);
-          *reinterpret_cast<intx4*>(kslot + klds(k, 2 * kc)) = lo;
-          *reinterpret_cast<intx4*>(kslot + klds(k, 2 * kc + 1)) = hi;
+        if (kFp8 && !kK8) {   // 16 codes -> bf16 chunks 2kc, 2kc + 1
+          const intx4 c = st[k];
+          *reinterpret_cast<intx4*>(kslot + klds(k, 2 * kc)) = e4m3x8_to_bf16(c.x, c.y);
+          *reinterpret_cast<intx4*>(kslot + klds(k, 2 * kc + 1)) = e4m3x8_to_bf16(c.z, c.w);
         } else {
           *reinterpret_cast<intx4*>(kslot + klds(k, kc)) = st[k];
         }
       }
-    } else if (kFp8) {
+    } else if (kFp8 && !kV8) {   // 16 keys -> bf16 chunks 2vc (keys 16vc ..) and 2vc + 1
       uint32_t keep_lo[4], keep_hi[4];
       keep_mask(key_rel - vc * 16, keep_lo);
       keep_mask(key_rel - vc * 16 - 8, keep_hi);
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
-        intx4 lo, hi;
-        e4m3x16_to_bf16(st[k], lo, hi);
-        const int row = vrow0 + 64 * k;
-        *reinterpret_cast<intx4*>(vslot + row * 128 + (((2 * vc) ^ xv_st) << 4)) = apply_keep(lo, keep_lo);
-        *reinterpret_cast<intx4*>(vslot + row * 128 + (((2 * vc + 1) ^ xv_st) << 4)) = apply_keep(hi, keep_hi);
+        const intx4 c = st[k];
+        *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc)) = apply_keep(e4m3x8_to_bf16(c.x, c.y), keep_lo);
+        *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc + 1)) = apply_keep(e4m3x8_to_bf16(c.z, c.w), keep_hi);
       }
     } else {
       uint32_t keep[4];
-      keep_mask(key_rel - vc * 8, keep);
+      if (kFp8)
+        keep_mask8(key_rel - vc * 16, keep);
+      else
+        keep_mask(key_rel - vc * 8, keep);
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k) {
-        const int row = vrow0 + 32 * k;
-        *reinterpret_cast<intx4*>(vslot + row * 128 + ((vc ^ xv_st) << 4)) = apply_keep(st[k], keep);
-      }
+      for (int k = 0; k < kPerThread; ++k) *reinterpret_cast<intx4*>(vslot + vlds(k, vc)) = apply_keep(st[k], keep);
     }
   };
 
@@ -253,24 +282,32 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   const int q4 = lane >> 4;    // K-group of this lane
   const int head = g * kG + hg * 16 + r;    // this lane's query head
 
-  if (t_begin >= t_end || (kDense && split * p.chunk_tiles >= p.max_blocks)) {
+  // A split without keys: zeros for a single-split slot; otherwise an empty
+  // partial (m = -inf) that still takes part in the merge.
+  const bool empty = t_begin >= t_end || (kDense && split * p.chunk_tiles >= p.max_blocks);
+  if (empty && p.splits == 1) {
     if (loader) return;
-    if (p.splits == 1) {   // empty slot: zeros
-      for (int ct = 0; ct < kD / 16; ++ct) {
-        const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
-        if (p.out_f32)
-          *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
-        else
-          *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
-      }
-    } else if (q4 == 0) {  // no keys in this split: an empty partial for the merge
-      const int64_t row = ((int64_t)bg * p.splits + split) * kG + hg * 16 + r;
-      *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{kNegInf, 0.f};
+    for (int ct = 0; ct < kD / 16; ++ct) {
+      const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
+      if (p.out_f32)
+        *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
+      else
+        *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
     }
     return;
   }
-  const int nt = t_end - t_begin;
+  const int nt = empty ? 0 : t_end - t_begin;
   nphase = 2 * nt;
+
+  // Online-softmax state of a compute lane (head `head`, channels
+  // 16ct + 4q4 .. +3 of O^T tile ct).
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  floatx4 acc[kD / 16];
+#pragma unroll
+  for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (!empty) {
 
   // Start-up: the loaders' first kStages phases are in flight (dense) or go
   // first; every thread fills part of the block-id cache (rows t_begin ..
@@ -337,17 +374,20 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     int q = 0;
     for (; q + 2 * kStages < nphase; q += kStages) group(q, std::true_type{});
     for (; q < nphase; q += kStages) group(q, std::false_type{});
-    return;
-  }
+  } else {
 
   // ---------------- compute waves ----------------
   const float qk_scale = p.scale * kLog2e * (kFp8 ? p.k_scale[g] : 1.f);
-  // Q fragments (B operand of S^T): this lane's head, channels 32c + 8q4 .. +7.
+  // Q fragments (B operand of S^T): this lane's head, channels 32c + 8q4 ..
+  // +7 (FP8: 64(c/2) + 16q4 + 8(c%2) .. +7).
   intx4 qf[kD / 32];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD + q4 * 8;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD;
 #pragma unroll
-    for (int c = 0; c < kD / 32; ++c) qf[c] = *reinterpret_cast<const intx4*>(qp + c * 32);
+    for (int c = 0; c < kD / 32; ++c) {
+      const int ch = kMap16 ? 64 * (c >> 1) + 16 * q4 + 8 * (c & 1) : 32 * c + 8 * q4;
+      qf[c] = *reinterpret_cast<const intx4*>(qp + ch);
+    }
   }
   lds_barrier();   // block ids and phase 0 visible
 
@@ -355,60 +395,94 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   // whose swizzle is r itself; fragment c (channels 32c + 8q4 .. +7) is
   // chunk (4c + q4) ^ r = 4c ^ (q4 ^ r), at byte (kfrag ^ (c << 6)) +
   // 512 (32(j/2) + 4(j%2)).
-  const uint32_t kfrag = (8 * (r >> 2) + (r & 3)) * 512 + ((q4 ^ r) << 4);
+  // FP8: row r of tile j is key 16(r/4) + 4j + r%4 (swizzle r again); code
+  // chunk 4u + q4 holds the operands of steps 2u and 2u + 1, at byte
+  // (kfrag ^ (u << 6)) + 1024 j.
+  const uint32_t kfrag = kK8 ? (16 * (r >> 2) + (r & 3)) * 256 + ((q4 ^ r) << 4)
+                             : (8 * (r >> 2) + (r & 3)) * 512 + ((q4 ^ r) << 4);
   // V^T operand of channel tile t, key step s: row 16t + r, chunk
-  // (4s + q4) ^ swz_v(r), at byte vfrag_s + 2048 t.
-  const uint32_t vfrag0 = r * 128 + ((q4 ^ swz_v(r)) << 4);
-  const uint32_t vfrag1 = r * 128 + (((4 + q4) ^ swz_v(r)) << 4);
+  // (4s + q4) ^ swz_v(r) (8-bit K map: 2q4 + s), at byte vfrag_s + 2048 t.
+  // 8-bit V^T: code chunk q4 ^ swz_v8(r) holds keys 16q4 .. +15, both
+  // steps, at vfrag0 + 1024 t.
+  const uint32_t vfrag0 = kV8 ? r * 64 + ((q4 ^ swz_v8(r)) << 4)
+                              : r * 128 + (((kMap16 ? 2 * q4 : q4) ^ swz_v(r)) << 4);
+  const uint32_t vfrag1 = r * 128 + (((kMap16 ? 2 * q4 + 1 : 4 + q4) ^ swz_v(r)) << 4);
 
-  float m_run = kNegInf;
-  float l_run = 0.f;
-  floatx4 acc[kD / 16];
-#pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
   intx4 pb[2];
 
   auto k_phase = [&](int key0) {
     uint32_t kb = kfrag;
     asm volatile("" : "+v"(kb));   // addresses formed here, not hoisted and kept live
     floatx4 st[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    intx4 a[kD / 32][4];
+    if constexpr (kK8) {
+      intx4 raw[kD / 64][4];
 #pragma unroll
-    for (int c = 0; c < kD / 32; ++c) {
-      const uint32_t a_off = kb ^ (c << 6);
+      for (int u = 0; u < kD / 64; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          raw[u][j] = *reinterpret_cast<const intx4*>(kslot + (kb ^ (u << 6)) + j * 1024);
+#pragma unroll
+      for (int u = 0; u < kD / 64; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].x, raw[u][j].y), qf[2 * u], st[j]);
+          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].z, raw[u][j].w), qf[2 * u + 1], st[j]);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    } else {
+      intx4 a[kD / 32][4];
+#pragma unroll
+      for (int c = 0; c < kD / 32; ++c) {
+        const uint32_t a_off = kb ^ (c << 6);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a[c][j] = *reinterpret_cast<const intx4*>(kslot + a_off + ((j >> 1) * 32 + (j & 1) * 4) * 512);
+      }
+#pragma unroll
+      for (int c = 0; c < kD / 32; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[j] = mfma_bf16_16x16x32(a[c][j], qf[c], st[j]);
+      // Software pipeline: operands of eight products in flight ahead of the
+      // matrix unit (the other wave on this SIMD is a loader).
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    // Lane values: tile j, element i is key key0 + 8q4 + 32(j/2) + 4(j%2) + i
+    // (FP8: key0 + 16q4 + 4j + i); those in [lo, L) are attended.  A page
+    // wholly inside [lo, L) (every page but the first and last of a slot)
+    // takes the branch without masks.
+    float sv[4][4];
+    const bool interior = key0 >= lo && key0 + kPage <= L;   // uniform
+    if (interior) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a[c][j] = *reinterpret_cast<const intx4*>(kslot + a_off + ((j >> 1) * 32 + (j & 1) * 4) * 512);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[j][i] = st[j][i] * qk_scale;
+    } else {
+      const int ebase = key0 + (kMap16 ? 16 : 8) * q4;
+      const int e_lo = lo - ebase, e_hi = L - ebase;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = kMap16 ? 4 * j + i : 32 * (j >> 1) + 4 * (j & 1) + i;
+          sv[j][i] = (e >= e_lo && e < e_hi) ? st[j][i] * qk_scale : kNegInf;
+        }
     }
+    float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
 #pragma unroll
-    for (int c = 0; c < kD / 32; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st[j] = mfma_bf16_16x16x32(a[c][j], qf[c], st[j]);
-    // Software pipeline: operands of eight products in flight ahead of the
-    // matrix unit (the other wave on this SIMD is a loader).
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    // Lane values: tile j, element i is key key0 + 32(j/2) + 8q4 + 4(j%2) + i;
-    // those in [lo, L) are attended.
-    const int ebase = key0 + 8 * q4;
-    const int e_lo = lo - ebase, e_hi = L - ebase;
-    float sv[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 32 * (j >> 1) + 4 * (j & 1) + i;
-        const float x = st[j][i] * qk_scale;
-        sv[j][i] = (e >= e_lo && e < e_hi) ? x : kNegInf;
-      }
-    float mx = kNegInf;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 1; j < 4; ++j)
       mx = fmaxf(mx, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
     mx = wave_max_xor16_32(mx);
     // Lazy max: keep the old reference unless this tile exceeds it by > 2^8.
@@ -421,17 +495,20 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       for (int ct = 0; ct < kD / 16; ++ct) acc[ct] *= alpha;
     }
     m_run = m_new;
+    // p = 2^(s - m); a head with no attended key yet (m = -inf, only on a
+    // masked page) gets p = 0 instead of 2^NaN.
+    const float m_sub = m_new == kNegInf ? 0.f : m_new;
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[j][i] = m_new == kNegInf ? 0.f : fast_exp2(sv[j][i] - m_new);
+        sv[j][i] = fast_exp2(sv[j][i] - m_sub);
         psum += sv[j][i];
       }
     l_run += psum;
-    // P^T B operands: keys 32s + 8q4 .. +7 come from tiles 2s (first four)
-    // and 2s + 1 (last four).
+    // P^T B operands: keys 32s + 8q4 .. +7 (FP8: 16q4 + 8s .. +7) come from
+    // tiles 2s (first four) and 2s + 1 (last four).
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       pb[s] = intx4{(int)pack_bf16x2(sv[2 * s][0], sv[2 * s][1]), (int)pack_bf16x2(sv[2 * s][2], sv[2 * s][3]),
@@ -440,6 +517,24 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   };
 
   auto v_phase = [&]() {
+    if constexpr (kV8) {
+      intx4 raw[kD / 16];
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) raw[ct] = *reinterpret_cast<const intx4*>(vslot + vfrag0 + ct * 1024);
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        acc[ct] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[ct].x, raw[ct].y), pb[0], acc[ct]);
+        acc[ct] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[ct].z, raw[ct].w), pb[1], acc[ct]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+      return;
+    }
     intx4 a[2][kD / 16];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -465,10 +560,13 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     lds_barrier();   // V^T tile t visible
     v_phase();
   }
+  }   // compute waves
+  }   // !empty
 
-  // ---- finish: this wave holds every key of its 16 heads ----
+  // ---- finish: a compute wave holds every key of its 16 heads ----
   const float l_tot = wave_sum_xor16_32(l_run);
   if (p.splits == 1) {
+    if (loader) return;
     const float inv = (kFp8 ? p.v_scale[g] : 1.f) / l_tot;
 #pragma unroll
     for (int ct = 0; ct < kD / 16; ++ct) {
@@ -480,30 +578,37 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) =
             intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
     }
-  } else {
-    const int64_t row = ((int64_t)bg * p.splits + split) * kG + hg * 16 + r;
-#pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct)
-      *reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4) = acc[ct];
-    if (q4 == 0) *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{m_run, l_tot};
+    return;
   }
+  // Split partial for the combine kernel.
+  if (loader) return;
+  const int64_t row = ((int64_t)bg * p.splits + split) * kG + hg * 16 + r;
+#pragma unroll
+  for (int ct = 0; ct < kD / 16; ++ct)
+    *reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4) = acc[ct];
+  if (q4 == 0) *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{m_run, l_tot};
 }
 
 }  // namespace
+
+// FP8 tiles in LDS: K stays 8-bit, V^T is widened by the loaders (the
+// compute waves widen every K operand they read, four times per tile; the
+// loaders widen each V^T code once).
+constexpr bool kFp8K8 = true, kFp8V8 = false;
 
 hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream) {
   dim3 grid(p.splits, p.batch * p.hkv);
   const bool dense = p.window == 0;
   if (fp8) {
     if (dense)
-      hipLaunchKernelGGL((mqa_decode_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((mqa_decode_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<false, true, kFp8K8, kFp8V8>), grid, dim3(kThreads), 0, stream, p);
   } else {
     if (dense)
-      hipLaunchKernelGGL((mqa_decode_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((mqa_decode_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<false, false, false, false>), grid, dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }

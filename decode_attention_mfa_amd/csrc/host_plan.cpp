@@ -101,7 +101,7 @@ DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus
   if (pl.splits > 1) {
     const size_t rows = (size_t)d->batch * d->num_kv_heads * pl.splits * group;
     pl.part_o_offset = 0;
-    pl.part_ml_offset = align_up(rows * d->head_dim * sizeof(float), kWorkspaceAlign);
+    pl.part_ml_offset = align_up(pl.part_o_offset + rows * d->head_dim * sizeof(float), kWorkspaceAlign);
     pl.workspace_bytes = align_up(pl.part_ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);
   }
   return pl;

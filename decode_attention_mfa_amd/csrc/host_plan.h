@@ -32,6 +32,7 @@ constexpr int32_t kMaxChunkPages = 2048;
 // Workspace regions are aligned to this many bytes.
 constexpr size_t kWorkspaceAlign = 256;
 
+
 // Validate sizes and dtypes (no pointers).  `mqa_entry` applies the MQA
 // entry's extra rule Hkv == 1.
 mfa_status validate_decode_desc(const mfa_decode_desc* d, int32_t window, bool mqa_entry);

@@ -57,6 +57,7 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
   if (pl.splits > 1) {
     p.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_offset);
     p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_ml_offset);
+
   }
   p.scale = scale;
   p.batch = d->batch;
