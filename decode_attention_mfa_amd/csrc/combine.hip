@@ -102,11 +102,113 @@ __global__ void __launch_bounds__(256) combine_any_kernel(DecodeParams p, int gr
         intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
 }
 
+// Balanced partition (one KV head, d = 256): slot b's pieces were computed
+// by workgroups w_lo .. w_hi (unit_desc[b]); workgroup w's partial for the
+// slot is 2w, except the first one's when the slot is that workgroup's last
+// piece (2w + 1).  A slot held by one workgroup already has its output, and
+// a slot without keys gets zeros here.  When every slot has the same page
+// count (a multiple of the split count), the cut is the split plan's: slot
+// b's pieces are workgroups b*S .. b*S+S-1, each its first piece; those
+// partials are loaded together with the descriptor (one memory round trip)
+// and merged like the split combine.  Otherwise pieces are merged in
+// increasing workgroup order, four loads at a time.
+template <int kMaxSplits>
+__global__ void __launch_bounds__(256) combine_balanced_kernel(DecodeParams p) {
+  constexpr int kD = 256;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // over B*Hq
+  if (row >= (int64_t)p.batch * p.hq) return;
+  const int b = (int)(row / p.hq);
+  const int h = (int)(row - (int64_t)b * p.hq);
+  const int ch = lane * 4;
+  const int S = p.splits;
+  const int L = slot_len(p.ctx_lens[b], p.max_blocks);
+  const intx4 dsc = *reinterpret_cast<const intx4*>(p.unit_desc + 4 * (int64_t)b);
+  floatx2 ml[kMaxSplits];
+  floatx4 o[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int64_t r = 2 * ((int64_t)b * S + min(s, S - 1)) * p.hq + h;
+    ml[s] = *reinterpret_cast<const floatx2*>(p.part_ml + r * 2);
+    o[s] = *reinterpret_cast<const floatx4*>(p.part_o + r * kD + ch);
+  }
+  // Every load above is in flight before the first branch: the compiler
+  // would otherwise sink each into the branch that uses it (three round
+  // trips instead of one).
+  asm volatile("" ::"v"(L), "v"(dsc.x), "v"(dsc.y), "v"(dsc.z));
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) asm volatile("" ::"v"(ml[s]), "v"(o[s]));
+  const int64_t off = ((int64_t)b * p.hq + h) * kD + ch;
+  if (L == 0) {
+    if (p.out_f32)
+      *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + off) = floatx4{0.f, 0.f, 0.f, 0.f};
+    else
+      *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + off) = intx2{0, 0};
+    return;
+  }
+  const int w_lo = dsc.x, w_hi = dsc.z;
+  if (w_lo >= w_hi) return;   // one workgroup held the whole slot
+  float M = kNegInf, lsum = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (S <= kMaxSplits && w_lo == b * S && w_hi == w_lo + S - 1 && dsc.y == 1) {
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < S) M = fmaxf(M, ml[s].x);
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < S && ml[s].x != kNegInf) {
+        const float wgt = fast_exp2(ml[s].x - M);
+        lsum += wgt * ml[s].y;
+        acc += wgt * o[s];
+      }
+    }
+  } else {
+    auto piece_of = [&](int w) -> int64_t { return 2 * (int64_t)w + ((w == w_lo && dsc.y == 0) ? 1 : 0); };
+    for (int w0 = w_lo; w0 <= w_hi; w0 += 4) {
+      floatx2 ml4[4];
+      floatx4 o4[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t r = piece_of(min(w0 + s, w_hi)) * p.hq + h;
+        ml4[s] = *reinterpret_cast<const floatx2*>(p.part_ml + r * 2);
+        o4[s] = *reinterpret_cast<const floatx4*>(p.part_o + r * kD + ch);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (w0 + s > w_hi || ml4[s].x == kNegInf) continue;
+        const float m_new = fmaxf(M, ml4[s].x);
+        const float a = M == kNegInf ? 0.f : fast_exp2(M - m_new);
+        const float wgt = fast_exp2(ml4[s].x - m_new);
+        lsum = a * lsum + wgt * ml4[s].y;
+        acc = a * acc + wgt * o4[s];
+        M = m_new;
+      }
+    }
+  }
+  const float inv = lsum > 0.f ? (p.v_scale ? p.v_scale[0] : 1.f) / lsum : 0.f;
+  const floatx4 v = acc * inv;
+  if (p.out_f32)
+    *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + off) = v;
+  else
+    *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + off) =
+        intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
+}
+
 }  // namespace
 
 hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.hkv * group;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (p.balanced) {
+    if (p.hkv != 1 || d != 256 || group != p.hq) return hipErrorInvalidValue;
+    if (p.splits <= 2)
+      hipLaunchKernelGGL(combine_balanced_kernel<2>, grid, block, 0, stream, p);
+    else if (p.splits <= 4)
+      hipLaunchKernelGGL(combine_balanced_kernel<4>, grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL(combine_balanced_kernel<8>, grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.splits <= 2)
     hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, p, group, d);
   else if (p.splits <= 4)

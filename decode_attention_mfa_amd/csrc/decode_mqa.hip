@@ -55,6 +55,9 @@ constexpr int kThreads = 512;          // 4 compute waves + 4 loader waves
 constexpr int kLoaders = 256;
 constexpr int kPhaseBytes = 32768;     // one bf16 K or V^T tile in LDS
 constexpr int kMaxChunkTiles = 2048;   // block ids cached per workgroup
+constexpr int kMaxBalancedSlots = 512; // balanced partition: slots per batch at most
+constexpr int kMaxBalancedTiles = 512; // and pages per workgroup at most
+constexpr int kMinBalancedPages = 4;   // pages per workgroup at least
 constexpr float kLazyRescale = 8.f;    // log2 headroom before the max moves
 
 // LDS swizzles (XOR on the 16-byte chunk index).  The 16 lanes reading one
@@ -125,10 +128,28 @@ using Int = std::integral_constant<int, N>;
 // compute waves widen their operands; otherwise the loaders widen the codes
 // to bf16 as they publish a phase.  8-bit K tiles use the key <-> row map
 // that lets one 16-byte read feed two products (see above).
-template <bool kDense, bool kFp8, bool kK8, bool kV8>
+//
+// kBal (paged, dense, one KV head): instead of cutting every slot into the
+// same number of chunks of its capacity, the workgroups of a 1-D grid split
+// the batch's actual pages evenly.  Slot b's pages are the global page range
+// [P_b, P_b + ceil(L_b/64)) with P_b the prefix sum over earlier slots; with
+// T pages in all and Ge active workgroups, workgroup w takes global pages
+// [wT/Ge, (w+1)T/Ge).  A workgroup thus walks one or more slot pieces back
+// to back: the loaders stream across piece boundaries and the compute waves
+// start a fresh softmax state and load the new slot's query at each one.  A
+// piece that is a whole slot writes its output; the others write partials
+// for the merge.  The compute waves work the partition out (synchronising
+// among themselves through an LDS counter) while the loaders already stream
+// the pages the split plan would give, which is the partition of a batch of
+// full slots.  The partition depends only on the lengths, so results are
+// reproducible.
+template <bool kDense, bool kFp8, bool kK8, bool kV8, bool kBal>
 __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   static_assert(kFp8 || (!kK8 && !kV8), "8-bit LDS tiles need an FP8 cache");
   static_assert(kK8 || !kV8, "8-bit V^T tiles use the 8-bit K key map");
+  static_assert(!kBal || kDense, "the balanced partition covers dense attention");
+  static_assert(kMaxBalancedSlots == 2 * kLoaders && kMaxBalancedTiles == 2 * kLoaders &&
+                kMaxBalancedTiles <= kMaxChunkTiles, "two slots and two tiles per compute thread");
   constexpr bool kMap16 = kK8;                          // key map of 8-bit K tiles
   constexpr int kElem = kFp8 ? 1 : 2;                 // bytes per cached element
   constexpr int kPerThread = kPhaseBytes * kElem / 2 / 16 / kLoaders;   // 16-byte loads per phase
@@ -141,15 +162,25 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t kslot[kKSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t vslot[kVSlot];
   __shared__ int blk_ids[kMaxChunkTiles];
+  // Balanced partition: first global page and length of every slot, each
+  // tile's (slot << 20 | page) and keys below the slot end, scan partials, a
+  // counter the compute waves synchronise on, and {tiles, speculation held}.
+  __shared__ int bal_first[kBal ? kMaxBalancedSlots : 1];
+  __shared__ int bal_len[kBal ? kMaxBalancedSlots : 1];
+  __shared__ int tile_pg[kBal ? kMaxBalancedTiles : 1];
+  __shared__ uint8_t tile_keys[kBal ? kMaxBalancedTiles : 1];
+  __shared__ int bal_wsum[kBal ? 4 : 1];
+  __shared__ int bal_sync[1];
+  __shared__ int bal_hdr[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const bool loader = wave >= 4;
-  const int bg = blockIdx.y;
-  const int b = bg / p.hkv;
+  const int bg = kBal ? 0 : blockIdx.y;
+  int b = bg / p.hkv;          // slot (changes per piece under the balanced partition)
   const int g = bg - b * p.hkv;
-  const int split = blockIdx.x;
+  const int split = kBal ? 0 : blockIdx.x;
   const int32_t* trow = p.block_table ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
 
   // Dense attention: the split's first page (split * chunk) does not depend
@@ -158,12 +189,21 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   // is known (a split that turns out to be past the end simply drops them).
   // With a window the first page moves with the length.
   int t_begin = kDense ? min(split * p.chunk_tiles, p.max_blocks - 1) : 0;
+  // Balanced partition: a batch whose slots all have the same number of
+  // pages, a multiple of the split count, is cut exactly like the split plan
+  // (workgroup w = slot w / splits, pages from (w % splits) * chunk), so
+  // those block ids are fetched alongside the lengths and used if the real
+  // partition agrees.
+  const int spec_b = kBal ? (int)blockIdx.x / p.splits : 0;
+  const int spec_pg = kBal ? ((int)blockIdx.x - spec_b * p.splits) * p.chunk_tiles : 0;
+  const int32_t* spec_row = kBal ? p.block_table + (int64_t)spec_b * p.max_blocks : trow;
   int blk_first[kFirstTiles];
 #pragma unroll
   for (int i = 0; i < kFirstTiles; ++i)
-    blk_first[i] = (kDense && trow && loader) ? trow[min(t_begin + i, p.max_blocks - 1)] : 0;
-  const int L = slot_len(p.ctx_lens[b], p.max_blocks);
+    blk_first[i] = (kDense && spec_row && (kBal || loader)) ? spec_row[min((kBal ? spec_pg : t_begin) + i, p.max_blocks - 1)] : 0;
+  int L = kBal ? 0 : slot_len(p.ctx_lens[b], p.max_blocks);
   int nphase = 0;   // two phases (K, V) per tile of this split; set once L is known
+  int bal_nt = 0;   // balanced partition: tiles of this workgroup
 
   // ---- loader state ----
   // Loader thread lt copies 16-byte chunks idx = lt + 256 k of a phase.
@@ -225,7 +265,8 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   // consecutive keys of one channel (vc*8 .. vc*8+7; FP8: 16 keys vc*16 ..).
   auto store_phase = [&](int ph, const intx4* st) {
     if (ph >= nphase) return;
-    const int key_rel = L - (t_begin + (ph >> 1)) * kPage;   // keys of this tile < L
+    // Keys of this tile below the slot end (read for V^T phases only).
+    auto keys_of = [&]() { return kBal ? (int)tile_keys[ph >> 1] : L - (t_begin + (ph >> 1)) * kPage; };
     if ((ph & 1) == 0) {
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
@@ -238,6 +279,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         }
       }
     } else if (kFp8 && !kV8) {   // 16 keys -> bf16 chunks 2vc (keys 16vc ..) and 2vc + 1
+      const int key_rel = keys_of();
       uint32_t keep_lo[4], keep_hi[4];
       keep_mask(key_rel - vc * 16, keep_lo);
       keep_mask(key_rel - vc * 16 - 8, keep_hi);
@@ -248,6 +290,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc + 1)) = apply_keep(e4m3x8_to_bf16(c.z, c.w), keep_hi);
       }
     } else {
+      const int key_rel = keys_of();
       uint32_t keep[4];
       if (kFp8)
         keep_mask8(key_rel - vc * 16, keep);
@@ -259,13 +302,157 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   };
 
   intx4 stage[kStages][kPerThread];
-  // The first kStages phases, block ids straight from the table.
-  auto load_first = [&]() {
+  // The first kStages phases, block ids straight from the table, or (balanced
+  // partition, other cut) from the tile list, clamped to its last tile.
+  auto load_first = [&](bool from_list) {
 #pragma unroll
     for (int ph = 0; ph < kStages; ++ph)
-      load_phase(ph, stage[ph], pool_block(readfirstlane(blk_first[ph >> 1]), p.num_blocks));
+      load_phase(ph, stage[ph],
+                 from_list ? readfirstlane(blk_ids[min(ph >> 1, bal_nt - 1)])
+                           : pool_block(readfirstlane(blk_first[ph >> 1]), p.num_blocks));
   };
-  if (kDense && loader) load_first();
+  if (kDense && !kBal && loader) load_first(false);
+
+  // ---- compute-wave identity ----
+  const int hg = wave & 3;     // head group: heads 16hg .. 16hg+15 of the KV group
+  const int r = lane & 15;     // MFMA row / column of this lane
+  const int q4 = lane >> 4;    // K-group of this lane
+  const int head = g * kG + hg * 16 + r;    // this lane's query head
+  // Q fragments (B operand of S^T): this lane's head, channels 32c + 8q4 ..
+  // +7 (FP8: 64(c/2) + 16q4 + 8(c%2) .. +7).
+  intx4 qf[kD / 32];
+  auto load_q = [&]() {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD;
+#pragma unroll
+    for (int c = 0; c < kD / 32; ++c) {
+      const int ch = kMap16 ? 64 * (c >> 1) + 16 * q4 + 8 * (c & 1) : 32 * c + 8 * q4;
+      qf[c] = *reinterpret_cast<const intx4*>(qp + ch);
+    }
+  };
+
+  // ---- balanced partition: this workgroup's slot pieces and tile list ----
+  if constexpr (kBal) {
+    if (tid == 0) bal_sync[0] = 0;
+    lds_barrier();   // counter ready
+    const int l_spec = slot_len(p.ctx_lens[spec_b], p.max_blocks);
+    const bool spec_issued = l_spec == p.max_blocks * kPage;
+    if (loader) {
+      // Speculation: the split plan's first pages, published as phase 0.
+      if (spec_issued) {
+        load_first(false);
+        nphase = 2;
+        store_phase(0, stage[0]);
+      }
+    } else {
+      b = spec_b;
+      load_q();
+      // Block ids of the split plan's pages for this workgroup, fetched
+      // with the lengths (tile i = tid + 256k); used where the partition
+      // agrees.
+      int spec_ids[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        spec_ids[k] = spec_row[min(spec_pg + tid + k * kLoaders, p.max_blocks - 1)];
+      // Four compute waves only: wait until all have passed sync point n.
+      auto cw_sync = [&](int n) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (lane == 0) __hip_atomic_fetch_add(bal_sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (__hip_atomic_load(bal_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 4 * n)
+          __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      };
+      // Thread t owns slots 2t and 2t+1: their lengths and pages, scanned.
+      const int s0 = 2 * tid, s1 = 2 * tid + 1;
+      const int raw0 = p.ctx_lens[min(s0, p.batch - 1)], raw1 = p.ctx_lens[min(s1, p.batch - 1)];
+      const int len0 = s0 < p.batch ? slot_len(raw0, p.max_blocks) : 0;
+      const int len1 = s1 < p.batch ? slot_len(raw1, p.max_blocks) : 0;
+      const int pg0 = (len0 + kPage - 1) / kPage, pg1 = (len1 + kPage - 1) / kPage;
+      int incl = pg0 + pg1;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int a = __shfl_up(incl, off);
+        if (lane >= off) incl += a;
+      }
+      if (lane == 63) bal_wsum[wave] = incl;
+      cw_sync(1);
+      int pre = 0, total = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int a = bal_wsum[w2];
+        if (w2 < wave) pre += a;
+        total += a;
+      }
+      const int first0 = pre + incl - pg0 - pg1, first1 = first0 + pg0;
+      bal_first[s0] = first0;
+      bal_first[s1] = first1;
+      bal_len[s0] = len0;
+      bal_len[s1] = len1;
+      const int ge = max(1, min((int)gridDim.x, total / kMinBalancedPages));
+      const int w = blockIdx.x;
+      const bool active = total > 0 && w < ge;
+      const int s_w = active ? (int)((int64_t)w * total / ge) : 0;
+      const int e_w = active ? (int)((int64_t)(w + 1) * total / ge) : 0;
+      // A slot whose first page falls in this range: tell the merge which
+      // workgroups hold its pieces (the last one holds its last page) and
+      // whether it is this workgroup's first piece.
+      auto describe = [&](int slot, int first, int pages) {
+        if (pages > 0 && first >= s_w && first < e_w) {
+          const int w_hi = (int)(((int64_t)(first + pages) * ge + total - 1) / total) - 1;
+          *reinterpret_cast<intx4*>(p.unit_desc + 4 * (int64_t)slot) = intx4{w, first == s_w ? 1 : 0, w_hi, 0};
+        }
+      };
+      describe(s0, first0, pg0);
+      describe(s1, first1, pg1);
+      cw_sync(2);
+      const int nt_here = min(e_w - s_w, kMaxBalancedTiles);
+      // Slot of global page x: the last slot starting at or before it.
+      auto slot_of = [&](int x) {
+        int lo_s = 0, hi_s = p.batch - 1;
+        while (lo_s < hi_s) {
+          const int mid = (lo_s + hi_s + 1) >> 1;
+          if (bal_first[mid] <= x) lo_s = mid; else hi_s = mid - 1;
+        }
+        return lo_s;
+      };
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = tid + k * kLoaders;
+        if (i < nt_here) {
+          const int x = s_w + i;
+          const int slot = slot_of(x);
+          const int page = x - bal_first[slot];
+          tile_pg[i] = (slot << 20) | page;
+          const bool spec_tile = slot == spec_b && page == spec_pg + i;
+          blk_ids[i] = pool_block(spec_tile ? spec_ids[k] : p.block_table[(int64_t)slot * p.max_blocks + page],
+                                  p.num_blocks);
+          tile_keys[i] = (uint8_t)min(kPage, bal_len[slot] - page * kPage);
+        }
+      }
+      const int b0 = nt_here > 0 ? readfirstlane(slot_of(s_w)) : spec_b;
+      const int spec_left = bal_first[spec_b] + (bal_len[spec_b] + kPage - 1) / kPage - s_w;
+      const bool spec_ok = spec_issued && nt_here >= kFirstTiles && b0 == spec_b &&
+                           s_w - bal_first[spec_b] == spec_pg && spec_left >= kFirstTiles;
+      if (tid == 0) {
+        bal_hdr[0] = nt_here;
+        bal_hdr[1] = spec_ok ? 1 : 0;
+      }
+      if (b0 != b) {
+        b = b0;
+        load_q();
+      }
+    }
+    lds_barrier();   // tile list, block ids, key counts and phase 0 visible
+    bal_nt = readfirstlane(bal_hdr[0]);
+    if (bal_nt == 0) return;
+    nphase = 2 * bal_nt;
+    if (!readfirstlane(bal_hdr[1])) {   // the speculation missed: phase 0 from the tile list
+      if (loader) {
+        load_first(true);
+        store_phase(0, stage[0]);
+      }
+      lds_barrier();
+    }
+  }
 
   const int lo = (!kDense && L > p.window) ? L - p.window : 0;
   int n_tiles = 0, t_lo = 0;
@@ -276,15 +463,9 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   if (!kDense) t_begin = t_lo + split * p.chunk_tiles;
   const int t_end = min(t_lo + n_tiles, t_begin + p.chunk_tiles);
 
-  // ---- compute-wave identity ----
-  const int hg = wave & 3;     // head group: heads 16hg .. 16hg+15 of the KV group
-  const int r = lane & 15;     // MFMA row / column of this lane
-  const int q4 = lane >> 4;    // K-group of this lane
-  const int head = g * kG + hg * 16 + r;    // this lane's query head
-
   // A split without keys: zeros for a single-split slot; otherwise an empty
   // partial (m = -inf) that still takes part in the merge.
-  const bool empty = t_begin >= t_end || (kDense && split * p.chunk_tiles >= p.max_blocks);
+  const bool empty = !kBal && (t_begin >= t_end || (kDense && split * p.chunk_tiles >= p.max_blocks));
   if (empty && p.splits == 1) {
     if (loader) return;
     for (int ct = 0; ct < kD / 16; ++ct) {
@@ -296,7 +477,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     }
     return;
   }
-  const int nt = empty ? 0 : t_end - t_begin;
+  const int nt = kBal ? bal_nt : (empty ? 0 : t_end - t_begin);
   nphase = 2 * nt;
 
   // Online-softmax state of a compute lane (head `head`, channels
@@ -306,6 +487,31 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   floatx4 acc[kD / 16];
 #pragma unroll
   for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // A compute wave holds every key of its 16 heads for the piece it has
+  // walked: the final output of slot b, or partial `piece` for the merge.
+  auto store_result = [&](bool final_out, int64_t piece) {
+    const float l_tot = wave_sum_xor16_32(l_run);
+    if (final_out) {
+      const float inv = (kFp8 ? p.v_scale[g] : 1.f) / l_tot;
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
+        const floatx4 v = acc[ct] * inv;
+        if (p.out_f32)
+          *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = v;
+        else
+          *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) =
+              intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
+      }
+      return;
+    }
+    const int64_t row = piece * kG + hg * 16 + r;
+#pragma unroll
+    for (int ct = 0; ct < kD / 16; ++ct)
+      *reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4) = acc[ct];
+    if (q4 == 0) *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{m_run, l_tot};
+  };
 
   if (!empty) {
 
@@ -319,23 +525,27 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < kFirstTiles; ++i)
       blk_first[i] = trow ? trow[min(t_begin + i, p.max_blocks - 1)] : 0;
-    load_first();
+    load_first(false);
   }
-  constexpr int kIdsPerThread = kMaxChunkTiles / kThreads;
-  const int32_t* btab = trow ? trow + t_begin : static_cast<const int32_t*>(p.ctx_lens);
-  int blk_cache[kIdsPerThread];
+  if constexpr (!kBal) {
+    constexpr int kIdsPerThread = kMaxChunkTiles / kThreads;
+    const int32_t* btab = trow ? trow + t_begin : static_cast<const int32_t*>(p.ctx_lens);
+    int blk_cache[kIdsPerThread];
 #pragma unroll
-  for (int k = 0; k < kIdsPerThread; ++k)
-    blk_cache[k] = btab[trow ? min(tid + k * kThreads, nt - 1) : 0];
+    for (int k = 0; k < kIdsPerThread; ++k)
+      blk_cache[k] = btab[trow ? min(tid + k * kThreads, nt - 1) : 0];
 #pragma unroll
-  for (int k = 0; k < kIdsPerThread; ++k) {
-    const int i = tid + k * kThreads;
-    if (i < nt) blk_ids[i] = pool_block(blk_cache[k], p.num_blocks);
+    for (int k = 0; k < kIdsPerThread; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < nt) blk_ids[i] = pool_block(blk_cache[k], p.num_blocks);
+    }
   }
 
   if (loader) {
-    store_phase(0, stage[0]);
-    lds_barrier();   // block ids and phase 0 visible
+    if constexpr (!kBal) {
+      store_phase(0, stage[0]);
+      lds_barrier();   // block ids and phase 0 visible
+    }
     // Phase kStages into the freed stage (clamped to the last tile, same K/V
     // parity, when the split is shorter; such a copy is never published).
     load_phase_cached(min(kStages, nphase - 2), stage[0]);
@@ -378,18 +588,10 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
 
   // ---------------- compute waves ----------------
   const float qk_scale = p.scale * kLog2e * (kFp8 ? p.k_scale[g] : 1.f);
-  // Q fragments (B operand of S^T): this lane's head, channels 32c + 8q4 ..
-  // +7 (FP8: 64(c/2) + 16q4 + 8(c%2) .. +7).
-  intx4 qf[kD / 32];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD;
-#pragma unroll
-    for (int c = 0; c < kD / 32; ++c) {
-      const int ch = kMap16 ? 64 * (c >> 1) + 16 * q4 + 8 * (c & 1) : 32 * c + 8 * q4;
-      qf[c] = *reinterpret_cast<const intx4*>(qp + ch);
-    }
+  if constexpr (!kBal) {
+    load_q();
+    lds_barrier();   // block ids and phase 0 visible
   }
-  lds_barrier();   // block ids and phase 0 visible
 
   // K operand of S^T tile j: row r is key 32(j/2) + 8(r/4) + 4(j%2) + r%4,
   // whose swizzle is r itself; fragment c (channels 32c + 8q4 .. +7) is
@@ -554,6 +756,38 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
+  if constexpr (kBal) {
+    // Tiles back to back; the loaders stream straight across piece
+    // boundaries.  A new piece (slot) starts a fresh state on its query.
+    // Piece 0 of a workgroup is partial 2w, its last piece 2w + 1.
+    int pg_first = 0, pg_last = 0, piece = 0;
+    for (int t = 0; t < nt; ++t) {
+      const int info = readfirstlane(tile_pg[t]);
+      const int slot = info >> 20, page = info & 0xfffff;
+      if (t == 0) {
+        L = readfirstlane(bal_len[slot]);
+        pg_first = page;
+      } else if (slot != b) {
+        store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, 2 * (int64_t)blockIdx.x + (piece > 0 ? 1 : 0));
+        ++piece;
+        b = slot;
+        load_q();
+        L = readfirstlane(bal_len[slot]);
+        pg_first = page;
+        m_run = kNegInf;
+        l_run = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      pg_last = page;
+      lds_barrier();   // K tile visible
+      k_phase(page * kPage);
+      lds_barrier();   // V^T tile visible
+      v_phase();
+    }
+    store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, 2 * (int64_t)blockIdx.x + (piece > 0 ? 1 : 0));
+    return;
+  }
   for (int t = 0; t < nt; ++t) {
     lds_barrier();   // K tile t visible
     k_phase((t_begin + t) * kPage);
@@ -563,30 +797,9 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   }   // compute waves
   }   // !empty
 
-  // ---- finish: a compute wave holds every key of its 16 heads ----
-  const float l_tot = wave_sum_xor16_32(l_run);
-  if (p.splits == 1) {
-    if (loader) return;
-    const float inv = (kFp8 ? p.v_scale[g] : 1.f) / l_tot;
-#pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
-      const floatx4 v = acc[ct] * inv;
-      if (p.out_f32)
-        *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = v;
-      else
-        *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) =
-            intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
-    }
-    return;
-  }
-  // Split partial for the combine kernel.
+  // ---- finish: the output, or this split's partial for the merge ----
   if (loader) return;
-  const int64_t row = ((int64_t)bg * p.splits + split) * kG + hg * 16 + r;
-#pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct)
-    *reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4) = acc[ct];
-  if (q4 == 0) *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{m_run, l_tot};
+  store_result(p.splits == 1, (int64_t)bg * p.splits + split);
 }
 
 }  // namespace
@@ -597,18 +810,29 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
 constexpr bool kFp8K8 = true, kFp8V8 = false;
 
 hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream) {
-  dim3 grid(p.splits, p.batch * p.hkv);
+  const dim3 grid(p.splits, p.batch * p.hkv);
   const bool dense = p.window == 0;
-  if (fp8) {
-    if (dense)
-      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8>), grid, dim3(kThreads), 0, stream, p);
+  if (p.balanced) {
+    // One workgroup per range of the batch's pages: as many as the split
+    // plan would use (the kernel leaves extra ones idle for short batches).
+    const dim3 grid1(p.splits * p.batch * p.hkv);
+    if (!dense || p.hkv != 1 || !p.block_table || p.batch > kMaxBalancedSlots ||
+        p.chunk_tiles > kMaxBalancedTiles || p.max_blocks > (1 << 20))
+      return hipErrorInvalidValue;
+    if (fp8)
+      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8, true>), grid1, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((mqa_decode_kernel<false, true, kFp8K8, kFp8V8>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false, true>), grid1, dim3(kThreads), 0, stream, p);
+  } else if (fp8) {
+    if (dense)
+      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8, false>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mqa_decode_kernel<false, true, kFp8K8, kFp8V8, false>), grid, dim3(kThreads), 0, stream, p);
   } else {
     if (dense)
-      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false, false>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((mqa_decode_kernel<false, false, false, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<false, false, false, false, false>), grid, dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -24,7 +24,8 @@ int path_for(int32_t group, int32_t d, int32_t kv) {
   return -1;
 }
 
-// FP8 storage: the shared-tile MQA kernel converts tiles on the way to LDS.
+// FP8 storage: only the shared-tile MQA kernel reads E4M3 codes (it widens
+// them to bf16 MFMA operands itself).
 bool fp8_supported(int path) { return path == (int)DecodePath::kMqaShared; }
 
 }  // namespace
@@ -98,11 +99,21 @@ DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus
   pl.splits = (int32_t)splits;
   pl.chunk_pages = (int32_t)chunk;
 
+  // Lengths live on the device, so a ragged batch cannot be planned here;
+  // with the heuristic split count, MQA dense calls let the kernel cut the
+  // batch's actual pages evenly instead (paged caches only, decided at the
+  // call).
+  pl.balanced = pl.splits > 1 && pl.path == DecodePath::kMqaShared && d->num_splits == 0 &&
+                window == 0 && d->num_kv_heads == 1 && d->batch <= kMaxBalancedSlots &&
+                pl.chunk_pages <= kMaxBalancedChunk && d->max_blocks_per_seq <= (1 << 20);
   if (pl.splits > 1) {
-    const size_t rows = (size_t)d->batch * d->num_kv_heads * pl.splits * group;
+    size_t rows = (size_t)d->batch * d->num_kv_heads * pl.splits * group;
+    if (pl.balanced) rows *= 2;   // two partials per workgroup
     pl.part_o_offset = 0;
     pl.part_ml_offset = align_up(pl.part_o_offset + rows * d->head_dim * sizeof(float), kWorkspaceAlign);
-    pl.workspace_bytes = align_up(pl.part_ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);
+    pl.unit_desc_offset = align_up(pl.part_ml_offset + rows * 2 * sizeof(float), kWorkspaceAlign);
+    const size_t desc_bytes = pl.balanced ? (size_t)d->batch * 4 * sizeof(int32_t) : 0;
+    pl.workspace_bytes = align_up(pl.unit_desc_offset + desc_bytes, kWorkspaceAlign);
   }
   return pl;
 }

@@ -24,6 +24,11 @@ struct DecodePlan {
   int32_t pages_cap;      // most pages one slot can touch
   size_t part_o_offset;   // bytes into the workspace
   size_t part_ml_offset;
+  // Paged calls split the batch's actual pages evenly over splits * B
+  // workgroups instead (MQA, dense, heuristic split count): room for two
+  // partials per workgroup and one int4 piece descriptor per slot.
+  bool balanced;
+  size_t unit_desc_offset;
   size_t workspace_bytes; // 0 when splits == 1
 };
 
@@ -31,6 +36,10 @@ struct DecodePlan {
 constexpr int32_t kMaxChunkPages = 2048;
 // Workspace regions are aligned to this many bytes.
 constexpr size_t kWorkspaceAlign = 256;
+// Balanced partition limits: one scan lane per slot (a 512-thread
+// workgroup) and at most this many pages per workgroup (piece list in LDS).
+constexpr int32_t kMaxBalancedSlots = 512;
+constexpr int32_t kMaxBalancedChunk = 512;
 
 
 // Validate sizes and dtypes (no pointers).  `mqa_entry` applies the MQA

@@ -26,6 +26,13 @@ struct DecodeParams {
   void* out;                  // [B, Hq, d]
   float* part_o;              // [B*Hkv, splits, G, d]   (splits > 1)
   float* part_ml;             // [B*Hkv, splits, G, 2]   (splits > 1)
+  // Balanced partition (MQA, paged, dense): the batch's pages are cut into
+  // equal ranges, one per workgroup of a 1-D grid; partials then live at
+  // rows 2w (the workgroup's first range piece) and 2w+1 (its last), and
+  // unit_desc[b] = {first workgroup, its piece is that workgroup's first (1)
+  // or last (0), last workgroup, 0} tells the merge where slot b's pieces are.
+  int32_t balanced;
+  int32_t* unit_desc;         // [B] int4
   float scale;                // logit scale
   int32_t batch;
   int32_t hq;

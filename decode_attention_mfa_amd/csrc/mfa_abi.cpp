@@ -57,7 +57,10 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
   if (pl.splits > 1) {
     p.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_offset);
     p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_ml_offset);
-
+    if (pl.balanced && block_table) {
+      p.balanced = 1;
+      p.unit_desc = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + pl.unit_desc_offset);
+    }
   }
   p.scale = scale;
   p.batch = d->batch;

@@ -98,7 +98,13 @@ typedef enum mfa_dtype {
  *                       BF16 or F32; kv F32 with q F32 and out F32
  *   num_splits          0 = choose with the library's heuristic
  *                       (mfa_decode_plan_splits); > 0 forces that many splits
- *                       of each slot's key range
+ *                       of each slot's key range.  With 0, a paged dense MQA
+ *                       call (Hkv == 1, B <= 512, at most 512 pages per
+ *                       split) instead spreads the batch's actual pages
+ *                       evenly over the same number of workgroups, reading
+ *                       ctx_lens on the device (ragged batches keep every
+ *                       compute unit busy); results then depend on the
+ *                       lengths only, and are bit-identical across runs.
  * Supported (Hq/Hkv, d): (64, 256) on the shared-tile MFMA path (MQA);
  * (16, 192), (16, 256) on the per-group MFMA path (GQA); any Hq/Hkv and any
  * d <= 256 that is a multiple of 4 with F32 storage.
@@ -156,7 +162,8 @@ mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
                                     size_t workspace_bytes, mfa_stream_t stream);
 
 /* Workspace bytes a call with this descriptor and window needs (0 when every
- * slot fits one split).  Pure host arithmetic: no HIP call is made when
+ * slot fits one split; room for the even page partition when num_splits is 0
+ * and the call may use it).  Pure host arithmetic: no HIP call is made when
  * desc->num_splits > 0; otherwise the current device's compute-unit count is
  * queried once and cached. */
 size_t mfa_decode_workspace_size(const mfa_decode_desc* desc, int32_t window);

@@ -137,3 +137,19 @@ def test_length_counts_the_current_token():
     shorter = run_decode(case, t, lens=torch.tensor([999], dtype=torch.int32, device="cuda"))
     assert not torch.equal(full, shorter)
     assert_parity(shorter, oracle(case, ctx_lens=np.array([999])), "bf16", "L-1")
+
+
+def test_balanced_partition_many_short_slots():
+    # Heuristic split count on a paged MQA batch: the workgroups divide the
+    # batch's actual pages, so one workgroup walks several short slots and
+    # long slots span several workgroups; empty slots sit in between.
+    lens = [1, 0, 63, 64, 65, 0, 130, 4096, 1, 2, 700, 0, 4033, 128, 129, 5, 3000, 64] * 2
+    case = make_decode_case(109, batch=len(lens), ctx_lens=lens, hq=64, hkv=1, d=256,
+                            scale=1 / 16)
+    t = to_device(case)
+    got = run_decode(case, t, num_splits=0).clone()
+    assert_parity(got, oracle(case), "bf16", "balanced partition")
+    for b in np.flatnonzero(np.array(lens) == 0):
+        assert torch.all(got[b] == 0)
+    again = run_decode(case, t, num_splits=0)
+    assert torch.equal(got.view(torch.int16), again.view(torch.int16))
