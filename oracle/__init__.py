@@ -21,6 +21,10 @@ What it computes, and which passage each function follows:
 * :func:`query_proj` -- the low-rank query path: down-projection to the
   2048 rank, normalisation, up-projection to 64 x 256 (Step-3 report,
   section 2).
+* :func:`kv_append` -- the step before decode attention: write each slot's
+  new K/V token at its current length and advance the length on the device
+  (duck-llm chapter 7, sections 7.5 and 7.6); :func:`e4m3fn_encode` is the
+  brute-force nearest-code FP8 encoder it uses for FP8 caches.
 * :mod:`oracle.codecs` -- bf16 and OCP FP8 E4M3 (E4M3FN) storage decoders.
 
 Pins (tests/test_oracle_*.py) tie every function to something other than
@@ -35,6 +39,7 @@ for the accounting model.
 from .codecs import bf16_bits_to_f64, e4m3fn_codes_to_f64, decode_storage
 from .attention import decode_attention
 from .query_proj import query_proj, rms_norm
+from .kv_append import e4m3fn_encode, kv_append
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -43,4 +48,6 @@ __all__ = [
     "decode_attention",
     "query_proj",
     "rms_norm",
+    "e4m3fn_encode",
+    "kv_append",
 ]
