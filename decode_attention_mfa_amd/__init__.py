@@ -8,6 +8,7 @@ from .binding import (
     mfa_decode_attention_gqa,
     mfa_decode_plan_splits,
     mfa_decode_workspace_size,
+    mfa_kv_append,
     mfa_query_proj,
 )
 
@@ -17,5 +18,6 @@ __all__ = [
     "mfa_decode_attention_gqa",
     "mfa_decode_plan_splits",
     "mfa_decode_workspace_size",
+    "mfa_kv_append",
     "mfa_query_proj",
 ]

@@ -22,6 +22,7 @@ EXPORTED = (
     "mfa_decode_attention_gqa",
     "mfa_decode_workspace_size",
     "mfa_decode_plan_splits",
+    "mfa_kv_append",
     "mfa_query_proj",
     "mfa_query_proj_workspace_size",
     "mfa_status_string",
@@ -42,6 +43,19 @@ class MfaDecodeDesc(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
+    ]
+
+
+class MfaKvAppendDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("new_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -87,6 +101,8 @@ def load():
     lib.mfa_decode_workspace_size.restype = ctypes.c_size_t
     lib.mfa_decode_plan_splits.argtypes = [desc_p, ctypes.c_int32, ctypes.c_int32]
     lib.mfa_decode_plan_splits.restype = ctypes.c_int32
+    lib.mfa_kv_append.argtypes = [ctypes.POINTER(MfaKvAppendDesc), P, P, P, P, P, P, P, P, P, P]
+    lib.mfa_kv_append.restype = ctypes.c_int
     lib.mfa_query_proj.argtypes = [qp_p, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.mfa_query_proj.restype = ctypes.c_int
     lib.mfa_query_proj_workspace_size.argtypes = [qp_p]

@@ -16,7 +16,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import MFA_BF16, MFA_F32, MFA_FP8_E4M3, MfaDecodeDesc, MfaQueryProjDesc, check
+from ._lib import (MFA_BF16, MFA_F32, MFA_FP8_E4M3, MfaDecodeDesc, MfaKvAppendDesc,
+                   MfaQueryProjDesc, check)
 
 PAGE = 64
 _workspaces = {}
@@ -129,6 +130,30 @@ def mfa_decode_attention_gqa(q, k_cache, v_cache, block_table, ctx_lens, out, sc
     """GQA / sliding-window decode attention; see mfa_decode_attention_gqa."""
     return _decode("gqa", q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_scale,
                    v_scale, window, num_splits, workspace, stream)
+
+
+def kv_append_desc(k_new, k_cache, block_table):
+    """Build an MfaKvAppendDesc from tensors (paged when block_table is given)."""
+    B, hkv, d = k_new.shape
+    if block_table is not None:
+        max_blocks, num_blocks = block_table.shape[1], k_cache.shape[0]
+    else:
+        max_blocks, num_blocks = k_cache.shape[1] // PAGE, 0
+    return MfaKvAppendDesc(batch=B, num_kv_heads=hkv, head_dim=d, page_size=PAGE,
+                           max_blocks_per_seq=max_blocks, num_blocks=num_blocks,
+                           new_dtype=_dtype_code(k_new),
+                           kv_dtype=_dtype_code(k_cache, allow_fp8=True))
+
+
+def mfa_kv_append(k_new, v_new, k_cache, v_cache, block_table, ctx_lens, *, k_scale=None,
+                  v_scale=None, active=None, stream=None):
+    """Append one token's K/V per slot and advance ctx_lens on the device; see
+    mfa_kv_append in the header."""
+    lib = _lib.load()
+    desc = kv_append_desc(k_new, k_cache, block_table)
+    check(lib.mfa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(k_scale),
+                            _ptr(v_scale), _ptr(active), _stream(k_new, stream)))
 
 
 def query_proj_desc(x, w_qup, q_out, num_heads, eps):

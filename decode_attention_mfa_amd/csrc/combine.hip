@@ -103,9 +103,9 @@ __global__ void __launch_bounds__(256) combine_any_kernel(DecodeParams p, int gr
 }
 
 // Balanced partition (one KV head, d = 256): slot b's pieces were computed
-// by workgroups w_lo .. w_hi (unit_desc[b]); workgroup w's partial for the
-// slot is 2w, except the first one's when the slot is that workgroup's last
-// piece (2w + 1).  A slot held by one workgroup already has its output, and
+// by workgroups w_lo .. w_hi (unit_desc[b]) of the G = S * B attention
+// workgroups; workgroup w's partial for the slot is w, except the first
+// one's when the slot is that workgroup's last piece (G + w).  A slot held by one workgroup already has its output, and
 // a slot without keys gets zeros here.  When every slot has the same page
 // count (a multiple of the split count), the cut is the split plan's: slot
 // b's pieces are workgroups b*S .. b*S+S-1, each its first piece; those
@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(256) combine_balanced_kernel(DecodeParams p) {
   floatx4 o[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
-    const int64_t r = 2 * ((int64_t)b * S + min(s, S - 1)) * p.hq + h;
+    const int64_t r = ((int64_t)b * S + min(s, S - 1)) * p.hq + h;
     ml[s] = *reinterpret_cast<const floatx2*>(p.part_ml + r * 2);
     o[s] = *reinterpret_cast<const floatx4*>(p.part_o + r * kD + ch);
   }
@@ -163,7 +163,8 @@ __global__ void __launch_bounds__(256) combine_balanced_kernel(DecodeParams p) {
       }
     }
   } else {
-    auto piece_of = [&](int w) -> int64_t { return 2 * (int64_t)w + ((w == w_lo && dsc.y == 0) ? 1 : 0); };
+    const int64_t G = (int64_t)S * p.batch;   // workgroups of the attention grid
+    auto piece_of = [&](int w) -> int64_t { return (w == w_lo && dsc.y == 0) ? G + w : w; };
     for (int w0 = w_lo; w0 <= w_hi; w0 += 4) {
       floatx2 ml4[4];
       floatx4 o4[4];

@@ -138,7 +138,7 @@ using Int = std::integral_constant<int, N>;
 // to back: the loaders stream across piece boundaries and the compute waves
 // start a fresh softmax state and load the new slot's query at each one.  A
 // piece that is a whole slot writes its output; the others write partials
-// for the merge.  The compute waves work the partition out (synchronising
+// for the merge (workgroup w's first piece to partial w, its last to G + w).  The compute waves work the partition out (synchronising
 // among themselves through an LDS counter) while the loaders already stream
 // the pages the split plan would give, which is the partition of a batch of
 // full slots.  The partition depends only on the lengths, so results are
@@ -334,11 +334,33 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   if constexpr (kBal) {
     if (tid == 0) bal_sync[0] = 0;
     lds_barrier();   // counter ready
+    // Speculation: if the first, the last and this workgroup's split-plan
+    // slot have the same length, take the batch to be uniform and predict
+    // the cut from that length alone (for full slots it is the split plan's
+    // own); the loaders publish the predicted first pages as phase 0 while
+    // the compute waves work out the real partition.
     const int l_spec = slot_len(p.ctx_lens[spec_b], p.max_blocks);
-    const bool spec_issued = l_spec == p.max_blocks * kPage;
+    const int l_first = slot_len(p.ctx_lens[0], p.max_blocks);
+    const int l_last = slot_len(p.ctx_lens[p.batch - 1], p.max_blocks);
+    const int p_spec = (l_spec + kPage - 1) / kPage;
+    const int tot_spec = p.batch * p_spec;
+    const int ge_spec = max(1, min((int)gridDim.x, tot_spec / kMinBalancedPages));
+    int pred_b = 0, pred_pg = 0;
+    bool spec_issued = false;
+    if (l_first == l_spec && l_last == l_spec && p_spec > 0 && (int)blockIdx.x < ge_spec) {
+      const int s_pred = (int)((int64_t)blockIdx.x * tot_spec / ge_spec);
+      const int e_pred = (int)((int64_t)(blockIdx.x + 1) * tot_spec / ge_spec);
+      pred_b = s_pred / p_spec;
+      pred_pg = s_pred - pred_b * p_spec;
+      spec_issued = e_pred - s_pred >= kFirstTiles && pred_pg + kFirstTiles <= p_spec;
+    }
     if (loader) {
-      // Speculation: the split plan's first pages, published as phase 0.
       if (spec_issued) {
+        if (pred_b != spec_b || pred_pg != spec_pg) {   // not the split plan's cut
+          const int32_t* row = p.block_table + (int64_t)pred_b * p.max_blocks;
+#pragma unroll
+          for (int i = 0; i < kFirstTiles; ++i) blk_first[i] = row[pred_pg + i];
+        }
         load_first(false);
         nphase = 2;
         store_phase(0, stage[0]);
@@ -429,9 +451,9 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         }
       }
       const int b0 = nt_here > 0 ? readfirstlane(slot_of(s_w)) : spec_b;
-      const int spec_left = bal_first[spec_b] + (bal_len[spec_b] + kPage - 1) / kPage - s_w;
-      const bool spec_ok = spec_issued && nt_here >= kFirstTiles && b0 == spec_b &&
-                           s_w - bal_first[spec_b] == spec_pg && spec_left >= kFirstTiles;
+      const int pred_left = bal_first[pred_b] + (bal_len[pred_b] + kPage - 1) / kPage - s_w;
+      const bool spec_ok = spec_issued && nt_here >= kFirstTiles && b0 == pred_b &&
+                           s_w - bal_first[pred_b] == pred_pg && pred_left >= kFirstTiles;
       if (tid == 0) {
         bal_hdr[0] = nt_here;
         bal_hdr[1] = spec_ok ? 1 : 0;
@@ -759,7 +781,8 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   if constexpr (kBal) {
     // Tiles back to back; the loaders stream straight across piece
     // boundaries.  A new piece (slot) starts a fresh state on its query.
-    // Piece 0 of a workgroup is partial 2w, its last piece 2w + 1.
+    // Piece 0 of workgroup w is partial w, its last piece partial G + w
+    // (G workgroups).
     int pg_first = 0, pg_last = 0, piece = 0;
     for (int t = 0; t < nt; ++t) {
       const int info = readfirstlane(tile_pg[t]);
@@ -768,7 +791,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         L = readfirstlane(bal_len[slot]);
         pg_first = page;
       } else if (slot != b) {
-        store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, 2 * (int64_t)blockIdx.x + (piece > 0 ? 1 : 0));
+        store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + blockIdx.x);
         ++piece;
         b = slot;
         load_q();
@@ -785,7 +808,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       lds_barrier();   // V^T tile visible
       v_phase();
     }
-    store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, 2 * (int64_t)blockIdx.x + (piece > 0 ? 1 : 0));
+    store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + blockIdx.x);
     return;
   }
   for (int t = 0; t < nt; ++t) {

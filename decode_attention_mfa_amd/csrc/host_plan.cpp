@@ -129,6 +129,28 @@ mfa_status validate_query_proj_desc(const mfa_query_proj_desc* d) {
   return MFA_OK;
 }
 
+mfa_status validate_kv_append(const mfa_kv_append_desc* d, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache, const int32_t* ctx_lens,
+                              const float* k_scale, const float* v_scale) {
+  if (!d) return MFA_ERR_NULL;
+  const bool combo = (d->new_dtype == MFA_BF16 && (d->kv_dtype == MFA_BF16 || d->kv_dtype == MFA_FP8_E4M3)) ||
+                     (d->new_dtype == MFA_F32 && d->kv_dtype == MFA_F32);
+  if (!combo) return MFA_ERR_DTYPE;
+  if (d->batch < 0 || d->num_kv_heads < 1 || d->head_dim < 4 || d->head_dim > 256 ||
+      d->head_dim % 4 || d->page_size != kPage || d->max_blocks_per_seq < 1)
+    return MFA_ERR_SHAPE;
+  if (d->batch == 0) return MFA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !ctx_lens) return MFA_ERR_NULL;
+  if (d->kv_dtype == MFA_FP8_E4M3 && (!k_scale || !v_scale)) return MFA_ERR_NULL;
+  const uintptr_t elem = d->kv_dtype == MFA_F32 ? 4 : d->kv_dtype == MFA_BF16 ? 2 : 1;
+  const uintptr_t new_elem = d->new_dtype == MFA_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % new_elem ||
+      (reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) % elem ||
+      reinterpret_cast<uintptr_t>(ctx_lens) % 4)
+    return MFA_ERR_ALIGN;
+  return MFA_OK;
+}
+
 QueryProjPlan plan_query_proj(const mfa_query_proj_desc* d) {
   QueryProjPlan pl{};
   // Split the hidden (K) dimension of the down projection so that it fills

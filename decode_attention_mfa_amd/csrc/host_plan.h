@@ -58,6 +58,11 @@ DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus
 
 mfa_status validate_query_proj_desc(const mfa_query_proj_desc* d);
 
+// Validate a KV-append descriptor and its pointers (nothing dereferenced).
+mfa_status validate_kv_append(const mfa_kv_append_desc* d, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache, const int32_t* ctx_lens,
+                              const float* k_scale, const float* v_scale);
+
 struct QueryProjPlan {
   int32_t k_splits;        // split-K factor of the down projection
   size_t y_partial_offset; // fp32 [k_splits, batch, rank]

@@ -27,8 +27,8 @@ struct DecodeParams {
   float* part_o;              // [B*Hkv, splits, G, d]   (splits > 1)
   float* part_ml;             // [B*Hkv, splits, G, 2]   (splits > 1)
   // Balanced partition (MQA, paged, dense): the batch's pages are cut into
-  // equal ranges, one per workgroup of a 1-D grid; partials then live at
-  // rows 2w (the workgroup's first range piece) and 2w+1 (its last), and
+  // equal ranges, one per workgroup of a 1-D grid of G; partials then live
+  // at rows w (the workgroup's first range piece) and G + w (its last), and
   // unit_desc[b] = {first workgroup, its piece is that workgroup's first (1)
   // or last (0), last workgroup, 0} tells the merge where slot b's pieces are.
   int32_t balanced;
@@ -50,6 +50,25 @@ struct DecodeParams {
   int64_t v_head_stride;
   int64_t v_row_stride;       // elements between consecutive channels
   int64_t v_seq_stride;       // contiguous V: elements between slots
+};
+
+// One KV-append launch (layouts as for DecodeParams with block_table set,
+// or the contiguous layouts when it is null).
+struct AppendParams {
+  const void* k_new;          // [B, Hkv, d]
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table; // nullptr: contiguous
+  int32_t* ctx_lens;          // [B], read and advanced
+  const float* k_scale;       // [Hkv] (FP8) or nullptr
+  const float* v_scale;
+  const int32_t* active;      // [B] or nullptr
+  int32_t batch;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t max_blocks;
+  int64_t num_blocks;
 };
 
 }  // namespace mfa

@@ -13,6 +13,7 @@ hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_gqa(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_f32(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream);
+hipError_t launch_kv_append(const AppendParams& p, int new_dtype, int kv_dtype, hipStream_t stream);
 mfa_status query_proj_enqueue(const mfa_query_proj_desc* d, const QueryProjPlan& pl,
                               const void* x, const void* w_down, const void* w_up,
                               const float* gain, void* q_out, void* workspace,
@@ -175,6 +176,34 @@ size_t mfa_decode_workspace_size(const mfa_decode_desc* desc, int32_t window) {
 int32_t mfa_decode_plan_splits(const mfa_decode_desc* desc, int32_t window, int32_t num_cus) {
   if (mfa::validate_decode_desc(desc, window, false) != MFA_OK) return 0;
   return mfa::plan_decode(desc, window, num_cus > 0 ? num_cus : 1).splits;
+}
+
+mfa_status mfa_kv_append(const mfa_kv_append_desc* desc, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_table,
+                         int32_t* ctx_lens, const float* k_scale, const float* v_scale,
+                         const int32_t* active, mfa_stream_t stream) {
+  mfa_status st = mfa::validate_kv_append(desc, k_new, v_new, k_cache, v_cache, ctx_lens, k_scale,
+                                          v_scale);
+  if (st != MFA_OK || desc->batch == 0) return st;
+  if (block_table && desc->num_blocks <= 0) return MFA_ERR_SHAPE;   // a paged call needs a pool
+  mfa::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.k_scale = desc->kv_dtype == MFA_FP8_E4M3 ? k_scale : nullptr;
+  p.v_scale = desc->kv_dtype == MFA_FP8_E4M3 ? v_scale : nullptr;
+  p.active = active;
+  p.batch = desc->batch;
+  p.hkv = desc->num_kv_heads;
+  p.head_dim = desc->head_dim;
+  p.max_blocks = desc->max_blocks_per_seq;
+  p.num_blocks = desc->num_blocks;
+  const hipError_t e = mfa::launch_kv_append(p, desc->new_dtype, desc->kv_dtype,
+                                             reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MFA_OK : MFA_ERR_LAUNCH;
 }
 
 mfa_status mfa_query_proj(const mfa_query_proj_desc* desc, const void* x, const void* w_qdown,

@@ -176,6 +176,65 @@ size_t mfa_decode_workspace_size(const mfa_decode_desc* desc, int32_t window);
 int32_t mfa_decode_plan_splits(const mfa_decode_desc* desc, int32_t window, int32_t num_cus);
 
 /*
+ * KV append with a device-owned length counter: the step just before decode
+ * attention in a decode loop (duck-llm chapter 7, section 7.6: the decode
+ * context kernel writes the new token's K/V and owns the active length, which
+ * then counts the token; section 7.5: state that lives on the device keeps a
+ * captured graph valid from step to step).
+ *   batch               B >= 0 slots (B == 0 enqueues nothing)
+ *   num_kv_heads        Hkv >= 1
+ *   head_dim            d, 4 <= d <= 256, multiple of 4
+ *   page_size           must be 64
+ *   max_blocks_per_seq  paged: length (= row stride) of each block-table row;
+ *                       contiguous: cache capacity / 64
+ *   num_blocks          paged: blocks in each pool (>= 1); contiguous: ignored
+ *   new_dtype           dtype of k_new / v_new: BF16 for BF16 or FP8_E4M3
+ *                       caches, F32 for F32 caches
+ *   kv_dtype            cache dtype: BF16, FP8_E4M3 or F32
+ */
+typedef struct mfa_kv_append_desc {
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int32_t new_dtype;
+  int32_t kv_dtype;
+} mfa_kv_append_desc;
+
+/*
+ * For every slot b, with pos = ctx_lens[b] read on the device:
+ *   K row pos of slot b, head g    <- k_new[b, g, :]
+ *   V column pos of slot b, head g <- v_new[b, g, :]
+ *   ctx_lens[b]                    <- pos + 1
+ * where row pos lives in block block_table[b, pos / 64] at row pos % 64
+ * (paged) or at position pos of slot b (contiguous), in the cache layouts of
+ * mfa_decode_attention (V channel-major).  BF16 and F32 values are copied
+ * bit for bit.  FP8: code = E4M3FN(x / scale) with the quotient taken in
+ * fp32, rounded to the nearest code (ties to the even code) and saturated to
+ * +-448; NaN stays NaN.
+ *   k_new, v_new   [B, Hkv, d] new_dtype, contiguous
+ *   k_cache, v_cache, block_table   as for mfa_decode_attention (block_table
+ *                  NULL: contiguous cache)
+ *   ctx_lens       [B] int32 on the device: read, then advanced by one
+ *   k_scale, v_scale   FP8 only: [Hkv] fp32 scales (stored = code * scale);
+ *                  NULL otherwise
+ *   active         NULL (every slot appends) or [B] int32, 0 = skip the slot
+ * A slot is left untouched (nothing written, length unchanged) when it is
+ * inactive, when pos < 0 or pos >= max_blocks_per_seq * 64, or (paged) when
+ * its block id lies outside [0, num_blocks).  One kernel is enqueued on
+ * `stream`; no allocation, no synchronisation, nothing read on the host, so
+ * the call can be captured in a graph together with the decode call.  Calls
+ * that share ctx_lens must be ordered on one stream.  Data pointers must be
+ * aligned to their element size.
+ */
+mfa_status mfa_kv_append(const mfa_kv_append_desc* desc, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_table,
+                         int32_t* ctx_lens, const float* k_scale, const float* v_scale,
+                         const int32_t* active, mfa_stream_t stream);
+
+/*
  * Low-rank MFA query path ("Step-3 is Large yet Affordable", section 2):
  *     y = x W_qdown^T;  r = y / sqrt(mean(y^2) + eps) * gain;  q = r W_qup^T
  * and q is viewed as [B, num_heads, head_dim] (head h = output columns

@@ -153,3 +153,16 @@ def test_balanced_partition_many_short_slots():
         assert torch.all(got[b] == 0)
     again = run_decode(case, t, num_splits=0)
     assert torch.equal(got.view(torch.int16), again.view(torch.int16))
+
+
+@pytest.mark.parametrize("length", [3000, 4033, 64])
+def test_balanced_partition_uniform_lengths(length):
+    # Every slot the same length below the table capacity: the kernel's
+    # predicted cut (from one slot's length) is the real one.
+    case = make_decode_case(110, batch=24, ctx_lens=[length] * 24, hq=64, hkv=1, d=256,
+                            scale=1 / 16, table_width=64)
+    t = to_device(case)
+    got = run_decode(case, t, num_splits=0).clone()
+    assert_parity(got, oracle(case), "bf16", f"uniform {length}")
+    again = run_decode(case, t, num_splits=0)
+    assert torch.equal(got.view(torch.int16), again.view(torch.int16))
