@@ -149,6 +149,10 @@ def main():
                     help="replay each step from a captured HIP graph instead of launching it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--with-append", action="store_true",
+                    help="each step appends one token per slot (mfa_kv_append, length "
+                         "advanced on the device) before the attention; lengths start "
+                         "steps+warmup below the workload's and grow to it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -188,9 +192,27 @@ def main():
         pools.append((t["k"].clone(), t["v"].clone()))
     out = t["out"]
     window = case.window
+    n_calls = max(args.warmup, len(pools)) + args.steps
+    if args.with_append:
+        # A decode loop: the device-side lengths start n_calls below the
+        # workload's and grow by one per step; the new tokens are fixed.
+        if args.graph:
+            raise SystemExit("--with-append times eager launches (graph warm-up replays would "
+                             "advance the lengths past the accounted ones)")
+        if window or np.min(case.ctx_lens) < n_calls:
+            raise SystemExit("--with-append needs a dense config with contexts >= steps + warmup")
+        t["lens"] = torch.from_numpy((case.ctx_lens - n_calls).astype(np.int32)).to(dev)
+        rng_new = np.random.default_rng(505)
+        from workloads import bf16_round_bits
+        new_kv = [torch.from_numpy(bf16_round_bits(rng_new.standard_normal(
+            (case.batch, case.hkv, case.d), dtype=np.float32)).view(np.int16)).view(
+            torch.bfloat16).to(dev) for _ in range(2)]
 
     def call(i):
         k, v = pools[i % len(pools)]
+        if args.with_append:
+            mfa.mfa_kv_append(new_kv[0], new_kv[1], k, v, t["table"], t["lens"],
+                              k_scale=t["k_scale"], v_scale=t["v_scale"])
         if case.hkv == 1 and window == 0:
             mfa.mfa_decode_attention(t["q"], k, v, t["table"], t["lens"], out, case.scale,
                                      k_scale=t["k_scale"], v_scale=t["v_scale"],
@@ -238,9 +260,21 @@ def main():
     call_ms = start.elapsed_time(end) / args.steps
 
     fmt_kv = case.kv_format
-    nbytes = accounting.decode_call_bytes(case.ctx_lens, hq=case.hq, hkv=case.hkv, d=case.d,
-                                          q_fmt="bf16", kv_fmt=fmt_kv, out_fmt=case.out_format,
-                                          window=window)
+    append_bytes = 0
+    if args.with_append:
+        # Lengths the timed steps' attention saw (after their appends), and
+        # the append's own bytes: new K/V read, cache rows written, lengths.
+        first = case.ctx_lens - n_calls + max(args.warmup, len(pools)) + 1
+        nbytes = float(np.mean([accounting.decode_call_bytes(
+            first + i, hq=case.hq, hkv=case.hkv, d=case.d, q_fmt="bf16", kv_fmt=fmt_kv,
+            out_fmt=case.out_format, window=window) for i in range(args.steps)]))
+        elem = {"bf16": 2, "e4m3": 1, "f32": 4}[fmt_kv]
+        append_bytes = case.batch * (2 * case.hkv * case.d * (2 + elem) + 8)
+        nbytes += append_bytes
+    else:
+        nbytes = accounting.decode_call_bytes(case.ctx_lens, hq=case.hq, hkv=case.hkv, d=case.d,
+                                              q_fmt="bf16", kv_fmt=fmt_kv,
+                                              out_fmt=case.out_format, window=window)
     flops = accounting.decode_call_flops(case.ctx_lens, hq=case.hq, d=case.d, window=window)
     achieved = nbytes / (call_ms * 1e-3) / 1e9
     desc = mfa.decode_desc(t["q"], t["k"], t["table"], out, args.num_splits)
@@ -261,20 +295,25 @@ def main():
         "dtype": {"bf16": "bf16", "e4m3": "fp8_e4m3 storage, bf16 MFMA", "f32": "f32"}[fmt_kv],
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "batch": case.batch,
-                   "ctx_len_mean": float(np.mean(case.ctx_lens)), "q_heads": case.hq,
+                   "ctx_len_mean": float(np.mean(case.ctx_lens) - (
+                       (n_calls - max(args.warmup, len(pools)) - 1 - (args.steps - 1) / 2)
+                       if args.with_append else 0.0)), "q_heads": case.hq,
                    "kv_heads": case.hkv, "head_dim": case.d, "kv_dtype": fmt_kv,
                    "page": 64, "window": window, "splits": splits, "kv_pool_copies": len(pools),
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": "hip graph replay" if args.graph else "eager",
+                   "append": bool(args.with_append)},
         "hbm_gbps": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "call_us_mean": call_ms * 1e3,
         "algorithmic_bytes_per_call": nbytes,
+        "append_bytes_per_call": append_bytes,
         "flops_per_call": flops,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(args.config),
                      "timed": "one HIP event pair around the timed steps on the launch "
                               "stream, divided by the step count (attention kernel + split "
-                              "merge kernel per step)"},
+                              "merge kernel per step" + (", after the KV append)" if
+                                                        args.with_append else ")")},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample of the same workload")

@@ -1,7 +1,7 @@
 // KV append with a device-owned length counter (duck-llm chapter 7, section
 // 7.6: the decode context kernel writes the new token's K/V and owns the
 // active length, which then counts the token).  One workgroup per slot: every
-// thread reads the slot's length, writes its channels of the new K row and V
+// thread reads the slot's length, writes its channel of the new K row and V
 // column for each KV head, and after a barrier (every thread has read the old
 // length) thread 0 advances the length.
 //
@@ -47,22 +47,36 @@ __device__ __forceinline__ float widen<uint16_t>(uint16_t v) {
 }
 
 // kKv: 0 = copy the new value's bits (bf16 -> bf16, f32 -> f32), 1 = E4M3FN.
+// Thread t owns channel t (d <= 256): its new K/V values, the slot's length
+// and its activity flag are all loaded before the first dependent step, so
+// the call costs two memory round trips (length, then block id) before the
+// writes.
 template <typename TNew, typename TKv, int kKv>
 __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
+  constexpr int kPre = 4;   // KV heads whose new values are loaded up front
   const int b = blockIdx.x;
-  if (p.active && p.active[b] == 0) return;
+  const int ch = threadIdx.x;
+  const int d = p.head_dim, hkv = p.hkv;
+  const TNew* kn = static_cast<const TNew*>(p.k_new) + (int64_t)b * hkv * d;
+  const TNew* vn = static_cast<const TNew*>(p.v_new) + (int64_t)b * hkv * d;
+  const bool mine = ch < d;
+  TNew kpre[kPre], vpre[kPre];
+#pragma unroll
+  for (int g = 0; g < kPre; ++g) {
+    const int i = min(g, hkv - 1) * d + min(ch, d - 1);
+    kpre[g] = kn[i];
+    vpre[g] = vn[i];
+  }
   const int pos = p.ctx_lens[b];
+  const int act = p.active ? p.active[b] : 1;
   const int64_t cap = (int64_t)p.max_blocks * kPage;
-  if (pos < 0 || pos >= cap) return;
+  if (act == 0 || pos < 0 || pos >= cap) return;
   const int row = pos & (kPage - 1);
   int64_t blk = 0;
   if (p.block_table) {
     blk = p.block_table[(int64_t)b * p.max_blocks + (pos >> 6)];
     if (blk < 0 || blk >= p.num_blocks) return;
   }
-  const int d = p.head_dim, hkv = p.hkv;
-  const TNew* kn = static_cast<const TNew*>(p.k_new) + (int64_t)b * hkv * d;
-  const TNew* vn = static_cast<const TNew*>(p.v_new) + (int64_t)b * hkv * d;
   TKv* kc = static_cast<TKv*>(p.k_cache);
   TKv* vc = static_cast<TKv*>(p.v_cache);
   for (int g = 0; g < hkv; ++g) {
@@ -73,14 +87,18 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
     const int64_t v_col = p.block_table ? (blk * hkv + g) * (int64_t)d * kPage + row
                                         : ((int64_t)b * hkv + g) * (int64_t)d * cap + pos;
     const int64_t v_stride = p.block_table ? kPage : cap;
-    const float ks = kKv == 1 ? p.k_scale[g] : 1.f;
-    const float vs = kKv == 1 ? p.v_scale[g] : 1.f;
-    for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
-      const TNew kv = kn[g * d + ch];
-      const TNew vv = vn[g * d + ch];
+    TNew kv, vv;
+    if (g < kPre) {
+      kv = kpre[g];
+      vv = vpre[g];
+    } else {
+      kv = kn[g * d + min(ch, d - 1)];
+      vv = vn[g * d + min(ch, d - 1)];
+    }
+    if (mine) {
       if constexpr (kKv == 1) {
-        kc[k_row + ch] = e4m3fn_encode(widen<TNew>(kv) / ks);
-        vc[v_col + ch * v_stride] = e4m3fn_encode(widen<TNew>(vv) / vs);
+        kc[k_row + ch] = e4m3fn_encode(widen<TNew>(kv) / p.k_scale[g]);
+        vc[v_col + ch * v_stride] = e4m3fn_encode(widen<TNew>(vv) / p.v_scale[g]);
       } else {
         kc[k_row + ch] = kv;
         vc[v_col + ch * v_stride] = vv;
@@ -88,7 +106,7 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
     }
   }
   __syncthreads();   // every thread has used the old length
-  if (threadIdx.x == 0) p.ctx_lens[b] = pos + 1;
+  if (ch == 0) p.ctx_lens[b] = pos + 1;
 }
 
 }  // namespace
