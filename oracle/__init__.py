@@ -25,6 +25,9 @@ What it computes, and which passage each function follows:
   new K/V token at its current length and advance the length on the device
   (duck-llm chapter 7, sections 7.5 and 7.6); :func:`e4m3fn_encode` is the
   brute-force nearest-code FP8 encoder it uses for FP8 caches.
+* :func:`decode_attention_mtp` -- several new query tokens per sequence (MTP
+  drafts or a speculative verify, Step-3 report section 5.2), causal among
+  themselves: token t of Tq attends the first L - (Tq - 1 - t) keys.
 * :mod:`oracle.codecs` -- bf16 and OCP FP8 E4M3 (E4M3FN) storage decoders.
 
 Pins (tests/test_oracle_*.py) tie every function to something other than
@@ -40,6 +43,7 @@ from .codecs import bf16_bits_to_f64, e4m3fn_codes_to_f64, decode_storage
 from .attention import decode_attention
 from .query_proj import query_proj, rms_norm
 from .kv_append import e4m3fn_encode, kv_append
+from .mtp import decode_attention_mtp, mtp_lengths
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -50,4 +54,6 @@ __all__ = [
     "rms_norm",
     "e4m3fn_encode",
     "kv_append",
+    "decode_attention_mtp",
+    "mtp_lengths",
 ]

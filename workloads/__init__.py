@@ -12,6 +12,7 @@ from .gen import (
     config_case,
     config_query_inputs,
     make_decode_case,
+    make_mtp_queries,
     make_query_inputs,
     ragged_lengths,
     CONFIG_NAMES,
@@ -24,6 +25,7 @@ __all__ = [
     "config_case",
     "config_query_inputs",
     "make_decode_case",
+    "make_mtp_queries",
     "make_query_inputs",
     "ragged_lengths",
     "CONFIG_NAMES",

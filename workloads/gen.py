@@ -229,6 +229,13 @@ def make_decode_case(seed, *, batch, ctx_lens, hq=64, hkv=1, d=256, kv_format="b
                       v_scale=v_scale)
 
 
+def make_mtp_queries(seed, *, batch, tq, hq=64, d=256, q_format="bf16"):
+    """Tq new query tokens per slot, [B, Tq, Hq, d], N(0, 1) in the query
+    storage format (multi-token decode: MTP drafts or a speculative verify)."""
+    rng = np.random.default_rng(seed)
+    return _storage(rng.standard_normal((batch, tq, hq, d), dtype=np.float32), q_format)
+
+
 def ragged_lengths(batch, *, p_lo=1024, p_hi=8192, geo_p=1.0 / 1024, cap=32768):
     """Continuous-batching context lengths: prefill length ~ Uniform{p_lo..p_hi}
     plus a decode index ~ Geometric(p) on {0, 1, ...} (numpy counts trials from 1,
