@@ -6,6 +6,7 @@ from .binding import (
     decode_desc,
     mfa_decode_attention,
     mfa_decode_attention_gqa,
+    mfa_decode_attention_mtp,
     mfa_decode_plan_splits,
     mfa_decode_workspace_size,
     mfa_kv_append,
@@ -16,6 +17,7 @@ __all__ = [
     "decode_desc",
     "mfa_decode_attention",
     "mfa_decode_attention_gqa",
+    "mfa_decode_attention_mtp",
     "mfa_decode_plan_splits",
     "mfa_decode_workspace_size",
     "mfa_kv_append",

@@ -20,7 +20,9 @@ MFA_F32, MFA_BF16, MFA_FP8_E4M3 = 0, 1, 2
 EXPORTED = (
     "mfa_decode_attention",
     "mfa_decode_attention_gqa",
+    "mfa_decode_attention_mtp",
     "mfa_decode_workspace_size",
+    "mfa_decode_mtp_workspace_size",
     "mfa_decode_plan_splits",
     "mfa_kv_append",
     "mfa_query_proj",
@@ -97,6 +99,11 @@ def load():
     lib.mfa_decode_attention_gqa.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float,
                                              ctypes.c_int32, P, ctypes.c_size_t, P]
     lib.mfa_decode_attention_gqa.restype = ctypes.c_int
+    lib.mfa_decode_attention_mtp.argtypes = [desc_p, ctypes.c_int32, P, P, P, P, P, P, P, P,
+                                             ctypes.c_float, P, ctypes.c_size_t, P]
+    lib.mfa_decode_attention_mtp.restype = ctypes.c_int
+    lib.mfa_decode_mtp_workspace_size.argtypes = [desc_p, ctypes.c_int32]
+    lib.mfa_decode_mtp_workspace_size.restype = ctypes.c_size_t
     lib.mfa_decode_workspace_size.argtypes = [desc_p, ctypes.c_int32]
     lib.mfa_decode_workspace_size.restype = ctypes.c_size_t
     lib.mfa_decode_plan_splits.argtypes = [desc_p, ctypes.c_int32, ctypes.c_int32]

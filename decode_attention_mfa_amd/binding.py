@@ -132,6 +132,36 @@ def mfa_decode_attention_gqa(q, k_cache, v_cache, block_table, ctx_lens, out, sc
                    v_scale, window, num_splits, workspace, stream)
 
 
+def mfa_decode_mtp_workspace_size(desc, num_query_tokens):
+    return int(_lib.load().mfa_decode_mtp_workspace_size(ctypes.byref(desc),
+                                                         int(num_query_tokens)))
+
+
+def mfa_decode_attention_mtp(q, k_cache, v_cache, block_table, ctx_lens, out, scale, *,
+                             k_scale=None, v_scale=None, num_splits=0, workspace=None,
+                             stream=None):
+    """Multi-token queries per slot: q and out [B, Tq, Hq, d], ctx_lens counting
+    all Tq new tokens; see mfa_decode_attention_mtp in the header."""
+    lib = _lib.load()
+    B, tq, hq, d = q.shape
+    key = ("mtp", tuple(q.shape), q.dtype, tuple(k_cache.shape), k_cache.dtype,
+           None if block_table is None else tuple(block_table.shape), out.dtype,
+           int(num_splits), q.device.index)
+    plan = _plans.get(key)
+    if plan is None:
+        desc = decode_desc(q[:, 0], k_cache, block_table, out[:, 0], num_splits)   # B sequences
+        plan = (desc, ctypes.byref(desc), mfa_decode_mtp_workspace_size(desc, tq))
+        _plans[key] = plan
+    _, desc_ref, need = plan
+    ws, ws_bytes = _workspace(q.device, need, workspace, "decode")
+    check(lib.mfa_decode_attention_mtp(desc_ref, ctypes.c_int32(tq), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
+                                       _ptr(k_scale), _ptr(v_scale), _ptr(out),
+                                       ctypes.c_float(scale), _ptr(ws), ctypes.c_size_t(ws_bytes),
+                                       _stream(q, stream)))
+    return out
+
+
 def kv_append_desc(k_new, k_cache, block_table):
     """Build an MfaKvAppendDesc from tensors (paged when block_table is given)."""
     B, hkv, d = k_new.shape

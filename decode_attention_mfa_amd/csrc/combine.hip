@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256) combine_balanced_kernel(DecodeParams p) {
   const int h = (int)(row - (int64_t)b * p.hq);
   const int ch = lane * 4;
   const int S = p.splits;
-  const int L = slot_len(p.ctx_lens[b], p.max_blocks);
+  const int L = query_len(p, b);
   const intx4 dsc = *reinterpret_cast<const intx4*>(p.unit_desc + 4 * (int64_t)b);
   floatx2 ml[kMaxSplits];
   floatx4 o[kMaxSplits];

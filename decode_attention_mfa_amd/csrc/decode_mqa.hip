@@ -37,6 +37,11 @@
 // 64(c/2) + 16(l/16) + 8(c%2) + e, S^T row r of tile j is key
 // 16(r/4) + 4j + r%4, and PV step s takes keys 16(l/16) + 8s + e.
 //
+// Multi-token queries ("Step-3 is Large yet Affordable", section 5.2, MTP):
+// a call with tq new tokens per cached sequence runs B * tq query slots;
+// slot s reads sequence s / tq's table row and attends its first
+// L - (tq - 1 - s % tq) keys, so the new tokens are causal among themselves.
+//
 // Online softmax in the log2 domain, fp32 state.  The running max only moves
 // when a tile's max exceeds it by more than kLazyRescale (2^8 headroom for
 // p = 2^(s - m) in fp32/bf16), so O is rescaled a handful of times per split;
@@ -181,7 +186,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   int b = bg / p.hkv;          // slot (changes per piece under the balanced partition)
   const int g = bg - b * p.hkv;
   const int split = kBal ? 0 : blockIdx.x;
-  const int32_t* trow = p.block_table ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
+  const int32_t* trow = p.block_table ? p.block_table + (int64_t)seq_of(p, b) * p.max_blocks : nullptr;
 
   // Dense attention: the split's first page (split * chunk) does not depend
   // on the slot length, so its block ids are fetched together with the
@@ -196,12 +201,12 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   // partition agrees.
   const int spec_b = kBal ? (int)blockIdx.x / p.splits : 0;
   const int spec_pg = kBal ? ((int)blockIdx.x - spec_b * p.splits) * p.chunk_tiles : 0;
-  const int32_t* spec_row = kBal ? p.block_table + (int64_t)spec_b * p.max_blocks : trow;
+  const int32_t* spec_row = kBal ? p.block_table + (int64_t)seq_of(p, spec_b) * p.max_blocks : trow;
   int blk_first[kFirstTiles];
 #pragma unroll
   for (int i = 0; i < kFirstTiles; ++i)
     blk_first[i] = (kDense && spec_row && (kBal || loader)) ? spec_row[min((kBal ? spec_pg : t_begin) + i, p.max_blocks - 1)] : 0;
-  int L = kBal ? 0 : slot_len(p.ctx_lens[b], p.max_blocks);
+  int L = kBal ? 0 : query_len(p, b);
   int nphase = 0;   // two phases (K, V) per tile of this split; set once L is known
   int bal_nt = 0;   // balanced partition: tiles of this workgroup
 
@@ -240,7 +245,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     const int tile = min(t_begin + (ph >> 1), p.max_blocks - 1);
     if ((ph & 1) == 0) {
       const char* base =
-          kpool + ((p.block_table ? (int64_t)blk : (int64_t)b * p.max_blocks + tile) * p.k_block_stride +
+          kpool + ((p.block_table ? (int64_t)blk : (int64_t)seq_of(p, b) * p.max_blocks + tile) * p.k_block_stride +
                    (int64_t)g * p.k_head_stride) * kElem + kgoff0;
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k)
@@ -248,7 +253,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     } else {
       const char* base =
           vpool + ((p.block_table ? (int64_t)blk * p.v_block_stride
-                                  : (int64_t)b * p.v_seq_stride + (int64_t)tile * kPage) +
+                                  : (int64_t)seq_of(p, b) * p.v_seq_stride + (int64_t)tile * kPage) +
                    (int64_t)g * p.v_head_stride) * kElem + vgoff0;
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k)
@@ -339,9 +344,9 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     // the cut from that length alone (for full slots it is the split plan's
     // own); the loaders publish the predicted first pages as phase 0 while
     // the compute waves work out the real partition.
-    const int l_spec = slot_len(p.ctx_lens[spec_b], p.max_blocks);
-    const int l_first = slot_len(p.ctx_lens[0], p.max_blocks);
-    const int l_last = slot_len(p.ctx_lens[p.batch - 1], p.max_blocks);
+    const int l_spec = query_len(p, spec_b);
+    const int l_first = query_len(p, 0);
+    const int l_last = query_len(p, p.batch - 1);
     const int p_spec = (l_spec + kPage - 1) / kPage;
     const int tot_spec = p.batch * p_spec;
     const int ge_spec = max(1, min((int)gridDim.x, tot_spec / kMinBalancedPages));
@@ -357,7 +362,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     if (loader) {
       if (spec_issued) {
         if (pred_b != spec_b || pred_pg != spec_pg) {   // not the split plan's cut
-          const int32_t* row = p.block_table + (int64_t)pred_b * p.max_blocks;
+          const int32_t* row = p.block_table + (int64_t)seq_of(p, pred_b) * p.max_blocks;
 #pragma unroll
           for (int i = 0; i < kFirstTiles; ++i) blk_first[i] = row[pred_pg + i];
         }
@@ -385,9 +390,9 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       };
       // Thread t owns slots 2t and 2t+1: their lengths and pages, scanned.
       const int s0 = 2 * tid, s1 = 2 * tid + 1;
-      const int raw0 = p.ctx_lens[min(s0, p.batch - 1)], raw1 = p.ctx_lens[min(s1, p.batch - 1)];
-      const int len0 = s0 < p.batch ? slot_len(raw0, p.max_blocks) : 0;
-      const int len1 = s1 < p.batch ? slot_len(raw1, p.max_blocks) : 0;
+      const int raw0 = query_len(p, min(s0, p.batch - 1)), raw1 = query_len(p, min(s1, p.batch - 1));
+      const int len0 = s0 < p.batch ? raw0 : 0;
+      const int len1 = s1 < p.batch ? raw1 : 0;
       const int pg0 = (len0 + kPage - 1) / kPage, pg1 = (len1 + kPage - 1) / kPage;
       int incl = pg0 + pg1;
 #pragma unroll
@@ -445,7 +450,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
           const int page = x - bal_first[slot];
           tile_pg[i] = (slot << 20) | page;
           const bool spec_tile = slot == spec_b && page == spec_pg + i;
-          blk_ids[i] = pool_block(spec_tile ? spec_ids[k] : p.block_table[(int64_t)slot * p.max_blocks + page],
+          blk_ids[i] = pool_block(spec_tile ? spec_ids[k] : p.block_table[(int64_t)seq_of(p, slot) * p.max_blocks + page],
                                   p.num_blocks);
           tile_keys[i] = (uint8_t)min(kPage, bal_len[slot] - page * kPage);
         }

@@ -40,6 +40,9 @@ constexpr size_t kWorkspaceAlign = 256;
 // workgroup) and at most this many pages per workgroup (piece list in LDS).
 constexpr int32_t kMaxBalancedSlots = 512;
 constexpr int32_t kMaxBalancedChunk = 512;
+// Query tokens per cached sequence a multi-token call takes at most (the
+// speculative / MTP verify widths the pages discuss are 2 to a few).
+constexpr int32_t kMaxQueryTokens = 16;
 
 
 // Validate sizes and dtypes (no pointers).  `mqa_entry` applies the MQA

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <climits>
 
 #include "host_plan.h"
 #include "kernel_params.h"
@@ -65,6 +66,7 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
   }
   p.scale = scale;
   p.batch = d->batch;
+  p.tq = 1;
   p.hq = d->num_q_heads;
   p.hkv = d->num_kv_heads;
   p.max_blocks = d->max_blocks_per_seq;
@@ -95,13 +97,31 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
   return p;
 }
 
-mfa_status decode_impl(const mfa_decode_desc* d, const void* q, const void* k_cache,
+// Descriptor of the query slots of a call with tq query tokens per cached
+// sequence: batch * tq slots, each with its own length (the kernels map a
+// slot back to its sequence).  tq > 1 is built for the shared-KV MQA path.
+mfa_status query_slot_desc(const mfa_decode_desc* d, int32_t tq, int32_t window, bool mqa_entry,
+                           mfa_decode_desc* vd) {
+  mfa_status st = mfa::validate_decode_desc(d, window, mqa_entry);
+  if (st != MFA_OK) return st;
+  if (tq < 1 || tq > mfa::kMaxQueryTokens || (int64_t)d->batch * tq > (int64_t)INT32_MAX)
+    return MFA_ERR_SHAPE;
+  *vd = *d;
+  vd->batch = d->batch * tq;
+  if (tq > 1 && mfa::plan_decode(vd, window, 1).path != mfa::DecodePath::kMqaShared)
+    return MFA_ERR_SHAPE;
+  return MFA_OK;
+}
+
+mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
                        const float* k_scale, const float* v_scale, void* out, float scale,
                        int32_t window, void* workspace, size_t workspace_bytes,
                        mfa_stream_t stream, bool mqa_entry) {
-  mfa_status st = mfa::validate_decode_desc(d, window, mqa_entry);
+  mfa_decode_desc vd;
+  mfa_status st = query_slot_desc(d0, tq, window, mqa_entry, &vd);
   if (st != MFA_OK) return st;
+  const mfa_decode_desc* d = &vd;
   if (d->batch == 0) return MFA_OK;
   st = mfa::validate_decode_ptrs(d, q, k_cache, v_cache, ctx_lens, k_scale, v_scale, out, scale);
   if (st != MFA_OK) return st;
@@ -117,8 +137,9 @@ mfa_status decode_impl(const mfa_decode_desc* d, const void* q, const void* k_ca
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return MFA_ERR_WORKSPACE;
 
-  const mfa::DecodeParams p = make_params(d, pl, q, k_cache, v_cache, block_table, ctx_lens,
-                                          k_scale, v_scale, out, scale, window, workspace);
+  mfa::DecodeParams p = make_params(d, pl, q, k_cache, v_cache, block_table, ctx_lens, k_scale,
+                                    v_scale, out, scale, window, workspace);
+  p.tq = tq;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   switch (pl.path) {
@@ -149,8 +170,30 @@ mfa_status mfa_decode_attention(const mfa_decode_desc* desc, const void* q, cons
                                 const int32_t* ctx_lens, const float* k_scale,
                                 const float* v_scale, void* out, float scale, void* workspace,
                                 size_t workspace_bytes, mfa_stream_t stream) {
-  return decode_impl(desc, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
+  return decode_impl(desc, 1, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
                      scale, 0, workspace, workspace_bytes, stream, /*mqa_entry=*/true);
+}
+
+mfa_status mfa_decode_attention_mtp(const mfa_decode_desc* desc, int32_t num_query_tokens,
+                                    const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    const float* k_scale, const float* v_scale, void* out,
+                                    float scale, void* workspace, size_t workspace_bytes,
+                                    mfa_stream_t stream) {
+  return decode_impl(desc, num_query_tokens, q, k_cache, v_cache, block_table, ctx_lens, k_scale,
+                     v_scale, out, scale, 0, workspace, workspace_bytes, stream,
+                     /*mqa_entry=*/true);
+}
+
+size_t mfa_decode_mtp_workspace_size(const mfa_decode_desc* desc, int32_t num_query_tokens) {
+  mfa_decode_desc vd;
+  if (query_slot_desc(desc, num_query_tokens, 0, true, &vd) != MFA_OK) return 0;
+  int cus = 0;
+  if (vd.num_splits == 0) {
+    cus = device_cu_count();
+    if (cus <= 0) return 0;
+  }
+  return mfa::plan_decode(&vd, 0, cus).workspace_bytes;
 }
 
 mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
@@ -159,7 +202,7 @@ mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
                                     const float* k_scale, const float* v_scale, void* out,
                                     float scale, int32_t window, void* workspace,
                                     size_t workspace_bytes, mfa_stream_t stream) {
-  return decode_impl(desc, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
+  return decode_impl(desc, 1, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
                      scale, window, workspace, workspace_bytes, stream, /*mqa_entry=*/false);
 }
 

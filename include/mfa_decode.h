@@ -150,6 +150,32 @@ mfa_status mfa_decode_attention(const mfa_decode_desc* desc, const void* q,
                                 mfa_stream_t stream);
 
 /*
+ * Multi-token queries per slot (MTP / speculative verification, "Step-3 is
+ * Large yet Affordable", section 5.2: MTP raises the attention's arithmetic
+ * intensity).  Each cached sequence b has num_query_tokens = Tq new query
+ * tokens, already appended: they are its last Tq cached keys, and token t
+ * attends keys [0, L_b - (Tq - 1 - t)), causal among the new tokens (a
+ * token with no key left gets zeros).  desc->batch counts sequences.
+ *   q            [B, Tq, Hq, d]        q_dtype, contiguous
+ *   out          [B, Tq, Hq, d]        out_dtype, written in full
+ *   ctx_lens     [B] int32, keys per sequence including all Tq new tokens
+ * Everything else as mfa_decode_attention (Hkv == 1, dense), with the
+ * workspace of mfa_decode_mtp_workspace_size(desc, Tq).  Built on the shared
+ * K/V path: bf16 or FP8 E4M3 caches, Hq = 64, d = 256; other shapes, or
+ * Tq outside [1, 16], return MFA_ERR_SHAPE.  Tq == 1 is mfa_decode_attention.
+ */
+mfa_status mfa_decode_attention_mtp(const mfa_decode_desc* desc, int32_t num_query_tokens,
+                                    const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    const float* k_scale, const float* v_scale, void* out,
+                                    float scale, void* workspace, size_t workspace_bytes,
+                                    mfa_stream_t stream);
+
+/* Workspace bytes of mfa_decode_attention_mtp with this descriptor and Tq
+ * (0 for an invalid descriptor); device queries as mfa_decode_workspace_size. */
+size_t mfa_decode_mtp_workspace_size(const mfa_decode_desc* desc, int32_t num_query_tokens);
+
+/*
  * GQA / sliding-window variant: as mfa_decode_attention, for any supported
  * Hkv (head h reads KV group floor(h / (Hq/Hkv))) and window >= 0
  * (0 = dense; W > 0 attends to keys [max(0, L - W), L - 1]).

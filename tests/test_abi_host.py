@@ -147,3 +147,27 @@ def test_forced_splits_are_honoured_up_to_the_page_count():
     for forced, expect in [(1, 1), (3, 3), (8, 8), (100, 64)]:
         d = desc(num_splits=forced)
         assert lib.mfa_decode_plan_splits(ctypes.byref(d), 0, 256) == expect
+
+
+def call_mtp(d, tq, ws=None, ws_bytes=0, q=A):
+    lib = _lib.load()
+    return lib.mfa_decode_attention_mtp(ctypes.byref(d), ctypes.c_int32(tq), q, A, A, A, A,
+                                        None, None, A, ctypes.c_float(0.0625), ws,
+                                        ctypes.c_size_t(ws_bytes), None)
+
+
+def test_multi_token_entry_rules():
+    lib = _lib.load()
+    assert call_mtp(desc(), 0) == MFA_ERR_SHAPE
+    assert call_mtp(desc(), 17) == MFA_ERR_SHAPE
+    assert call_mtp(desc(num_kv_heads=2, num_q_heads=128), 2) == MFA_ERR_SHAPE   # Hkv == 1
+    # fp32 MFA shapes run on the scalar path, which has no multi-token variant
+    assert call_mtp(desc(q_dtype=MFA_F32, kv_dtype=MFA_F32, out_dtype=MFA_F32), 2) == MFA_ERR_SHAPE
+    assert call_mtp(desc(), 2) == MFA_ERR_WORKSPACE               # forced splits need room
+    assert call_mtp(desc(), 2, q=None) == MFA_ERR_NULL
+    assert call_mtp(desc(batch=0), 3, q=None) == 0
+    # The workspace of Tq tokens is that of Tq times as many single-token slots.
+    for tq in (1, 2, 4):
+        got = lib.mfa_decode_mtp_workspace_size(ctypes.byref(desc(num_splits=4)), tq)
+        assert got == lib.mfa_decode_workspace_size(ctypes.byref(desc(batch=64 * tq, num_splits=4)), 0)
+    assert lib.mfa_decode_mtp_workspace_size(ctypes.byref(desc()), 0) == 0
