@@ -56,8 +56,7 @@ namespace {
 
 constexpr int kD = 256;
 constexpr int kG = 64;
-constexpr int kThreads = 512;          // 4 compute waves + 4 loader waves
-constexpr int kLoaders = 256;
+constexpr int kLoaders = 256;          // four loader waves (plus 4 or 8 compute waves)
 constexpr int kPhaseBytes = 32768;     // one bf16 K or V^T tile in LDS
 constexpr int kMaxChunkTiles = 2048;   // block ids cached per workgroup
 constexpr int kMaxBalancedSlots = 512; // balanced partition: slots per batch at most
@@ -148,13 +147,26 @@ using Int = std::integral_constant<int, N>;
 // the pages the split plan would give, which is the partition of a batch of
 // full slots.  The partition depends only on the lengths, so results are
 // reproducible.
-template <bool kDense, bool kFp8, bool kK8, bool kV8, bool kBal>
-__global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
+//
+// kTps = 2 (multi-token queries, an even number per sequence): a query slot
+// is a pair of consecutive new tokens, 128 query rows over one cache row, so
+// each K/V tile is read once for both.  Eight compute waves (wave w: token
+// w/4 of the pair, heads 16(w%4) ..) and the four loaders, 12 waves; the
+// first token of the pair attends one key fewer than the second.
+template <bool kDense, bool kFp8, bool kK8, bool kV8, bool kBal, int kTps>
+__global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(DecodeParams p) {
   static_assert(kFp8 || (!kK8 && !kV8), "8-bit LDS tiles need an FP8 cache");
   static_assert(kK8 || !kV8, "8-bit V^T tiles use the 8-bit K key map");
   static_assert(!kBal || kDense, "the balanced partition covers dense attention");
-  static_assert(kMaxBalancedSlots == 2 * kLoaders && kMaxBalancedTiles == 2 * kLoaders &&
-                kMaxBalancedTiles <= kMaxChunkTiles, "two slots and two tiles per compute thread");
+  static_assert(kTps == 1 || (kTps == 2 && kDense), "token pairs are built for dense attention");
+  constexpr int kCw = 4 * kTps;                       // compute waves
+  constexpr int kCt = 64 * kCw;                       // compute threads
+  constexpr int kNt = kCt + kLoaders;                 // threads
+  constexpr int kRows = kG * kTps;                    // query rows per slot and KV group
+  constexpr int kSpt = kMaxBalancedSlots / kCt;       // balanced partition: slots
+  constexpr int kTpt = kMaxBalancedTiles / kCt;       // and tiles per compute thread
+  static_assert(kSpt * kCt == kMaxBalancedSlots && kTpt * kCt == kMaxBalancedTiles &&
+                kMaxBalancedTiles <= kMaxChunkTiles, "slots and tiles split evenly over compute threads");
   constexpr bool kMap16 = kK8;                          // key map of 8-bit K tiles
   constexpr int kElem = kFp8 ? 1 : 2;                 // bytes per cached element
   constexpr int kPerThread = kPhaseBytes * kElem / 2 / 16 / kLoaders;   // 16-byte loads per phase
@@ -167,6 +179,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t kslot[kKSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t vslot[kVSlot];
   __shared__ int blk_ids[kMaxChunkTiles];
+  __shared__ intx4 qlds[kTps == 2 ? kCw * (kD / 32) * 64 : 1];   // token pairs: Q fragments
   // Balanced partition: first global page and length of every slot, each
   // tile's (slot << 20 | page) and keys below the slot end, scan partials, a
   // counter the compute waves synchronise on, and {tiles, speculation held}.
@@ -174,14 +187,14 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   __shared__ int bal_len[kBal ? kMaxBalancedSlots : 1];
   __shared__ int tile_pg[kBal ? kMaxBalancedTiles : 1];
   __shared__ uint8_t tile_keys[kBal ? kMaxBalancedTiles : 1];
-  __shared__ int bal_wsum[kBal ? 4 : 1];
+  __shared__ int bal_wsum[kBal ? kCw : 1];
   __shared__ int bal_sync[1];
   __shared__ int bal_hdr[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool loader = wave >= 4;
+  const bool loader = wave >= kCw;
   const int bg = kBal ? 0 : blockIdx.y;
   int b = bg / p.hkv;          // slot (changes per piece under the balanced partition)
   const int g = bg - b * p.hkv;
@@ -320,11 +333,15 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
 
   // ---- compute-wave identity ----
   const int hg = wave & 3;     // head group: heads 16hg .. 16hg+15 of the KV group
+  const int tk = kTps == 1 ? 0 : (wave >> 2);   // token of a pair
   const int r = lane & 15;     // MFMA row / column of this lane
   const int q4 = lane >> 4;    // K-group of this lane
-  const int head = g * kG + hg * 16 + r;    // this lane's query head
+  const int head = g * kRows + tk * kG + hg * 16 + r;    // this lane's query row
   // Q fragments (B operand of S^T): this lane's head, channels 32c + 8q4 ..
   // +7 (FP8: 64(c/2) + 16q4 + 8(c%2) .. +7).
+  // With token pairs (twelve waves, 168 registers per lane) each compute
+  // wave parks its fragments in its own LDS rows and reads them back per K
+  // tile, so that they are not held across the V phase.
   intx4 qf[kD / 32];
   auto load_q = [&]() {
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD;
@@ -333,6 +350,16 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       const int ch = kMap16 ? 64 * (c >> 1) + 16 * q4 + 8 * (c & 1) : 32 * c + 8 * q4;
       qf[c] = *reinterpret_cast<const intx4*>(qp + ch);
     }
+    if constexpr (kTps == 2) {
+#pragma unroll
+      for (int c = 0; c < kD / 32; ++c) qlds[(wave * (kD / 32) + c) * 64 + lane] = qf[c];
+    }
+  };
+  auto qfrag = [&](int c) {
+    if constexpr (kTps == 1)
+      return qf[c];
+    else
+      return qlds[(wave * (kD / 32) + c) * 64 + lane];
   };
 
   // ---- balanced partition: this workgroup's slot pieces and tile list ----
@@ -374,27 +401,32 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       b = spec_b;
       load_q();
       // Block ids of the split plan's pages for this workgroup, fetched
-      // with the lengths (tile i = tid + 256k); used where the partition
+      // with the lengths (tile i = tid + kCt k); used where the partition
       // agrees.
-      int spec_ids[2];
+      int spec_ids[kTpt];
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        spec_ids[k] = spec_row[min(spec_pg + tid + k * kLoaders, p.max_blocks - 1)];
-      // Four compute waves only: wait until all have passed sync point n.
+      for (int k = 0; k < kTpt; ++k)
+        spec_ids[k] = spec_row[min(spec_pg + tid + k * kCt, p.max_blocks - 1)];
+      // The compute waves only: wait until all have passed sync point n.
       auto cw_sync = [&](int n) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         if (lane == 0) __hip_atomic_fetch_add(bal_sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        while (__hip_atomic_load(bal_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 4 * n)
+        while (__hip_atomic_load(bal_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kCw * n)
           __builtin_amdgcn_s_sleep(1);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       };
-      // Thread t owns slots 2t and 2t+1: their lengths and pages, scanned.
-      const int s0 = 2 * tid, s1 = 2 * tid + 1;
-      const int raw0 = query_len(p, min(s0, p.batch - 1)), raw1 = query_len(p, min(s1, p.batch - 1));
-      const int len0 = s0 < p.batch ? raw0 : 0;
-      const int len1 = s1 < p.batch ? raw1 : 0;
-      const int pg0 = (len0 + kPage - 1) / kPage, pg1 = (len1 + kPage - 1) / kPage;
-      int incl = pg0 + pg1;
+      // Thread t owns slots kSpt t .. kSpt t + kSpt - 1: their lengths and
+      // pages, scanned.
+      int len[kSpt], pg[kSpt];
+      int incl = 0;
+#pragma unroll
+      for (int k = 0; k < kSpt; ++k) {
+        const int sk = kSpt * tid + k;
+        const int raw = query_len(p, min(sk, p.batch - 1));
+        len[k] = sk < p.batch ? raw : 0;
+        pg[k] = (len[k] + kPage - 1) / kPage;
+        incl += pg[k];
+      }
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int a = __shfl_up(incl, off);
@@ -404,16 +436,22 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       cw_sync(1);
       int pre = 0, total = 0;
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
+      for (int w2 = 0; w2 < kCw; ++w2) {
         const int a = bal_wsum[w2];
         if (w2 < wave) pre += a;
         total += a;
       }
-      const int first0 = pre + incl - pg0 - pg1, first1 = first0 + pg0;
-      bal_first[s0] = first0;
-      bal_first[s1] = first1;
-      bal_len[s0] = len0;
-      bal_len[s1] = len1;
+      int first[kSpt];
+      first[0] = pre + incl;
+#pragma unroll
+      for (int k = 0; k < kSpt; ++k) first[0] -= pg[k];
+#pragma unroll
+      for (int k = 1; k < kSpt; ++k) first[k] = first[k - 1] + pg[k - 1];
+#pragma unroll
+      for (int k = 0; k < kSpt; ++k) {
+        bal_first[kSpt * tid + k] = first[k];
+        bal_len[kSpt * tid + k] = len[k];
+      }
       const int ge = max(1, min((int)gridDim.x, total / kMinBalancedPages));
       const int w = blockIdx.x;
       const bool active = total > 0 && w < ge;
@@ -422,14 +460,14 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       // A slot whose first page falls in this range: tell the merge which
       // workgroups hold its pieces (the last one holds its last page) and
       // whether it is this workgroup's first piece.
-      auto describe = [&](int slot, int first, int pages) {
-        if (pages > 0 && first >= s_w && first < e_w) {
-          const int w_hi = (int)(((int64_t)(first + pages) * ge + total - 1) / total) - 1;
-          *reinterpret_cast<intx4*>(p.unit_desc + 4 * (int64_t)slot) = intx4{w, first == s_w ? 1 : 0, w_hi, 0};
+#pragma unroll
+      for (int k = 0; k < kSpt; ++k) {
+        if (pg[k] > 0 && first[k] >= s_w && first[k] < e_w) {
+          const int w_hi = (int)(((int64_t)(first[k] + pg[k]) * ge + total - 1) / total) - 1;
+          *reinterpret_cast<intx4*>(p.unit_desc + 4 * (int64_t)(kSpt * tid + k)) =
+              intx4{w, first[k] == s_w ? 1 : 0, w_hi, 0};
         }
-      };
-      describe(s0, first0, pg0);
-      describe(s1, first1, pg1);
+      }
       cw_sync(2);
       const int nt_here = min(e_w - s_w, kMaxBalancedTiles);
       // Slot of global page x: the last slot starting at or before it.
@@ -442,8 +480,8 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         return lo_s;
       };
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int i = tid + k * kLoaders;
+      for (int k = 0; k < kTpt; ++k) {
+        const int i = tid + k * kCt;
         if (i < nt_here) {
           const int x = s_w + i;
           const int slot = slot_of(x);
@@ -482,6 +520,10 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   }
 
   const int lo = (!kDense && L > p.window) ? L - p.window : 0;
+  // Keys this compute wave's token attends: the slot's (its last token's)
+  // length, one fewer for the first token of a pair.
+  auto query_keys = [&](int len) { return kTps == 1 ? len : max(len - (kTps - 1 - tk), 0); };
+  int Lq = query_keys(L);
   int n_tiles = 0, t_lo = 0;
   if (L > 0) {
     t_lo = lo / kPage;
@@ -520,7 +562,8 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   auto store_result = [&](bool final_out, int64_t piece) {
     const float l_tot = wave_sum_xor16_32(l_run);
     if (final_out) {
-      const float inv = (kFp8 ? p.v_scale[g] : 1.f) / l_tot;
+      // (The first token of a pair may have no key at all: zeros.)
+      const float inv = (kTps == 1 || l_tot > 0.f) ? (kFp8 ? p.v_scale[g] : 1.f) / l_tot : 0.f;
 #pragma unroll
       for (int ct = 0; ct < kD / 16; ++ct) {
         const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
@@ -533,7 +576,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       }
       return;
     }
-    const int64_t row = piece * kG + hg * 16 + r;
+    const int64_t row = piece * kRows + (head - g * kRows);
 #pragma unroll
     for (int ct = 0; ct < kD / 16; ++ct)
       *reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4) = acc[ct];
@@ -555,15 +598,15 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     load_first(false);
   }
   if constexpr (!kBal) {
-    constexpr int kIdsPerThread = kMaxChunkTiles / kThreads;
+    constexpr int kIdsPerThread = (kMaxChunkTiles + kNt - 1) / kNt;
     const int32_t* btab = trow ? trow + t_begin : static_cast<const int32_t*>(p.ctx_lens);
     int blk_cache[kIdsPerThread];
 #pragma unroll
     for (int k = 0; k < kIdsPerThread; ++k)
-      blk_cache[k] = btab[trow ? min(tid + k * kThreads, nt - 1) : 0];
+      blk_cache[k] = btab[trow ? min(tid + k * kNt, nt - 1) : 0];
 #pragma unroll
     for (int k = 0; k < kIdsPerThread; ++k) {
-      const int i = tid + k * kThreads;
+      const int i = tid + k * kNt;
       if (i < nt) blk_ids[i] = pool_block(blk_cache[k], p.num_blocks);
     }
   }
@@ -638,6 +681,11 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
   const uint32_t vfrag1 = r * 128 + (((kMap16 ? 2 * q4 + 1 : 4 + q4) ^ swz_v(r)) << 4);
 
   intx4 pb[2];
+  // LDS operand reads issued ahead of the products (16-byte reads; FP8 K
+  // reads feed two products each).  Twelve-wave workgroups leave the order
+  // to the compiler's register-pressure-aware scheduler.
+  constexpr int kAhead = 8;
+  constexpr int kAhead8 = 6;
 
   auto k_phase = [&](int key0) {
     uint32_t kb = kfrag;
@@ -654,16 +702,18 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       for (int u = 0; u < kD / 64; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].x, raw[u][j].y), qf[2 * u], st[j]);
-          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].z, raw[u][j].w), qf[2 * u + 1], st[j]);
+          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].x, raw[u][j].y), qfrag(2 * u), st[j]);
+          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].z, raw[u][j].w), qfrag(2 * u + 1), st[j]);
         }
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      if constexpr (kTps == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead8, 0);
 #pragma unroll
-      for (int i = 0; i < 10; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < 16 - kAhead8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead8, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
     } else {
       intx4 a[kD / 32][4];
 #pragma unroll
@@ -676,23 +726,26 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < kD / 32; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st[j] = mfma_bf16_16x16x32(a[c][j], qf[c], st[j]);
-      // Software pipeline: operands of eight products in flight ahead of the
-      // matrix unit (the other wave on this SIMD is a loader).
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        for (int j = 0; j < 4; ++j) st[j] = mfma_bf16_16x16x32(a[c][j], qfrag(c), st[j]);
+      // Software pipeline: operands of kAhead products in flight ahead of
+      // the matrix unit (the other wave on this SIMD is a loader; with token
+      // pairs, also the other token's compute wave).
+      if constexpr (kTps == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-      for (int i = 0; i < 24; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < 32 - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     // Lane values: tile j, element i is key key0 + 8q4 + 32(j/2) + 4(j%2) + i
     // (FP8: key0 + 16q4 + 4j + i); those in [lo, L) are attended.  A page
     // wholly inside [lo, L) (every page but the first and last of a slot)
     // takes the branch without masks.
     float sv[4][4];
-    const bool interior = key0 >= lo && key0 + kPage <= L;   // uniform
+    const bool interior = key0 >= lo && key0 + kPage <= Lq;   // uniform
     if (interior) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -700,7 +753,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         for (int i = 0; i < 4; ++i) sv[j][i] = st[j][i] * qk_scale;
     } else {
       const int ebase = key0 + (kMap16 ? 16 : 8) * q4;
-      const int e_lo = lo - ebase, e_hi = L - ebase;
+      const int e_lo = lo - ebase, e_hi = Lq - ebase;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -755,13 +808,15 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         acc[ct] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[ct].x, raw[ct].y), pb[0], acc[ct]);
         acc[ct] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[ct].z, raw[ct].w), pb[1], acc[ct]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      if constexpr (kTps == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead8, 0);
 #pragma unroll
-      for (int i = 0; i < 10; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < 16 - kAhead8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead8, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       return;
     }
     intx4 a[2][kD / 16];
@@ -774,13 +829,15 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = mfma_bf16_16x16x32(a[s][ct], pb[s], acc[ct]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    if constexpr (kTps == 1) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 32 - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   if constexpr (kBal) {
@@ -794,6 +851,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
       const int slot = info >> 20, page = info & 0xfffff;
       if (t == 0) {
         L = readfirstlane(bal_len[slot]);
+        Lq = query_keys(L);
         pg_first = page;
       } else if (slot != b) {
         store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + blockIdx.x);
@@ -801,6 +859,7 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
         b = slot;
         load_q();
         L = readfirstlane(bal_len[slot]);
+        Lq = query_keys(L);
         pg_first = page;
         m_run = kNegInf;
         l_run = 0.f;
@@ -837,30 +896,43 @@ __global__ void __launch_bounds__(kThreads) mqa_decode_kernel(DecodeParams p) {
 // loaders widen each V^T code once).
 constexpr bool kFp8K8 = true, kFp8V8 = false;
 
-hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream) {
+template <int kTps>
+void launch_mqa_t(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream) {
+  const dim3 block(256 * kTps + kLoaders);
   const dim3 grid(p.splits, p.batch * p.hkv);
-  const bool dense = p.window == 0;
   if (p.balanced) {
     // One workgroup per range of the batch's pages: as many as the split
     // plan would use (the kernel leaves extra ones idle for short batches).
     const dim3 grid1(p.splits * p.batch * p.hkv);
-    if (!dense || p.hkv != 1 || !p.block_table || p.batch > kMaxBalancedSlots ||
-        p.chunk_tiles > kMaxBalancedTiles || p.max_blocks > (1 << 20))
-      return hipErrorInvalidValue;
     if (fp8)
-      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8, true>), grid1, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8, true, kTps>), grid1, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false, true>), grid1, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false, true, kTps>), grid1, block, 0, stream, p);
   } else if (fp8) {
     if (dense)
-      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8, false>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((mqa_decode_kernel<false, true, kFp8K8, kFp8V8, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, true, kFp8K8, kFp8V8, false, kTps>), grid, block, 0, stream, p);
+    else if constexpr (kTps == 1)
+      hipLaunchKernelGGL((mqa_decode_kernel<false, true, kFp8K8, kFp8V8, false, 1>), grid, block, 0, stream, p);
   } else {
     if (dense)
-      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false, false>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((mqa_decode_kernel<false, false, false, false, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mqa_decode_kernel<true, false, false, false, false, kTps>), grid, block, 0, stream, p);
+    else if constexpr (kTps == 1)
+      hipLaunchKernelGGL((mqa_decode_kernel<false, false, false, false, false, 1>), grid, block, 0, stream, p);
+  }
+}
+
+hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream) {
+  const bool dense = p.window == 0;
+  if (p.balanced && (!dense || p.hkv != 1 || !p.block_table || p.batch > kMaxBalancedSlots ||
+                     p.chunk_tiles > kMaxBalancedTiles || p.max_blocks > (1 << 20)))
+    return hipErrorInvalidValue;
+  // Token pairs: one KV head, dense, 128 query rows per slot.
+  if (p.tps == 2) {
+    if (!dense || p.hkv != 1 || p.hq != 2 * kG) return hipErrorInvalidValue;
+    launch_mqa_t<2>(p, fp8, dense, stream);
+  } else {
+    if (p.tps != 1 || p.hq != kG * p.hkv) return hipErrorInvalidValue;
+    launch_mqa_t<1>(p, fp8, dense, stream);
   }
   return hipGetLastError();
 }

@@ -61,19 +61,21 @@ __device__ __forceinline__ int slot_len(int L, int max_blocks) {
   return min(max(L, 0), max_blocks * 64);
 }
 
-// Query slot s of a call with p.tq query tokens per cached sequence: its
-// cached sequence (table row, length entry), and the keys it attends: the
-// sequence's length, clamped as above, less the tq - 1 - s % tq tokens that
-// follow the query token (never below 0).
+// Query slot s of a call with p.tq query tokens per cached sequence, p.tps
+// of them per slot: its cached sequence (table row, length entry), and the
+// keys its last token attends: the sequence's length, clamped as above, less
+// the tokens that follow it (never below 0).
 template <class P>
 __device__ __forceinline__ int seq_of(const P& p, int s) {
-  return p.tq == 1 ? s : s / p.tq;
+  return p.tq == p.tps ? s : s / (p.tq / p.tps);
 }
 template <class P>
 __device__ __forceinline__ int query_len(const P& p, int s) {
   if (p.tq == 1) return slot_len(p.ctx_lens[s], p.max_blocks);
-  const int seq = s / p.tq;
-  return max(slot_len(p.ctx_lens[seq], p.max_blocks) - (p.tq - 1 - (s - seq * p.tq)), 0);
+  const int per_seq = p.tq / p.tps;
+  const int seq = s / per_seq;
+  const int last = (s - seq * per_seq) * p.tps + p.tps - 1;
+  return max(slot_len(p.ctx_lens[seq], p.max_blocks) - (p.tq - 1 - last), 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

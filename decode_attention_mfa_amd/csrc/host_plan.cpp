@@ -70,7 +70,8 @@ mfa_status validate_decode_ptrs(const mfa_decode_desc* d, const void* q, const v
   return MFA_OK;
 }
 
-DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus) {
+DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus,
+                       int32_t rows_per_head) {
   DecodePlan pl{};
   const int32_t group = d->num_q_heads / d->num_kv_heads;
   pl.path = (DecodePath)path_for(group, d->head_dim, d->kv_dtype);
@@ -107,7 +108,7 @@ DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus
                 window == 0 && d->num_kv_heads == 1 && d->batch <= kMaxBalancedSlots &&
                 pl.chunk_pages <= kMaxBalancedChunk && d->max_blocks_per_seq <= (1 << 20);
   if (pl.splits > 1) {
-    size_t rows = (size_t)d->batch * d->num_kv_heads * pl.splits * group;
+    size_t rows = (size_t)d->batch * d->num_kv_heads * pl.splits * group * rows_per_head;
     if (pl.balanced) rows *= 2;   // two partials per workgroup
     pl.part_o_offset = 0;
     pl.part_ml_offset = align_up(pl.part_o_offset + rows * d->head_dim * sizeof(float), kWorkspaceAlign);

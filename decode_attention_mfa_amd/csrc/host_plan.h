@@ -57,7 +57,10 @@ mfa_status validate_decode_ptrs(const mfa_decode_desc* d, const void* q, const v
 
 // Path, split count and workspace layout for a valid descriptor.  num_cus is
 // only used when desc->num_splits == 0.
-DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus);
+// rows_per_head: query rows per (slot, query head) of the descriptor, 2 when
+// each slot carries a pair of query tokens (the partials double).
+DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus,
+                       int32_t rows_per_head = 1);
 
 mfa_status validate_query_proj_desc(const mfa_query_proj_desc* d);
 

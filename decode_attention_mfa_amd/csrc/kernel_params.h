@@ -15,10 +15,11 @@ constexpr int kPage = 64;          // tokens per cache block (one kernel tile)
 // with block = block_table[b * max_blocks + t]; for a contiguous cache the
 // block index is replaced by (b * max_blocks + t) for K and the V tile starts
 // at v + b * v_seq_stride + g * v_head_stride + t * 64.
-// Query slot s is query token s % tq of cached sequence s / tq (block-table
-// row, length, contiguous cache slot).  With tq > 1 the tq tokens are the
-// last tq cached keys of their sequence and token t attends the first
-// L - (tq - 1 - t) keys (causal among the new tokens).
+// Query slot s holds tps consecutive query tokens of cached sequence
+// s / (tq / tps) (block-table row, length, contiguous cache slot).  With
+// tq > 1 the tq tokens are the last tq cached keys of their sequence and
+// token t attends the first L - (tq - 1 - t) keys (causal among the new
+// tokens); a slot's length is that of its last token.
 struct DecodeParams {
   const void* q;              // [B, Hq, d]  (B = batch query slots)
   const void* k;
@@ -40,6 +41,7 @@ struct DecodeParams {
   float scale;                // logit scale
   int32_t batch;              // query slots: cached sequences x tq
   int32_t tq;                 // query tokens per cached sequence (>= 1)
+  int32_t tps;                // query tokens per slot: 1, or 2 (pairs, hq = 2 x 64 rows)
   int32_t hq;
   int32_t hkv;
   int32_t max_blocks;         // block-table row length / capacity in blocks

@@ -67,6 +67,7 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
   p.scale = scale;
   p.batch = d->batch;
   p.tq = 1;
+  p.tps = 1;
   p.hq = d->num_q_heads;
   p.hkv = d->num_kv_heads;
   p.max_blocks = d->max_blocks_per_seq;
@@ -98,16 +99,19 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
 }
 
 // Descriptor of the query slots of a call with tq query tokens per cached
-// sequence: batch * tq slots, each with its own length (the kernels map a
-// slot back to its sequence).  tq > 1 is built for the shared-KV MQA path.
+// sequence.  An even tq > 1 runs batch * tq / 2 slots of two tokens each (one
+// K/V read per pair, 2 x Hq query rows per slot); an odd one batch * tq
+// single-token slots.  The kernels map a slot back to its sequence and give
+// each token its own length.  tq > 1 is built for the shared-KV MQA path.
 mfa_status query_slot_desc(const mfa_decode_desc* d, int32_t tq, int32_t window, bool mqa_entry,
-                           mfa_decode_desc* vd) {
+                           mfa_decode_desc* vd, int32_t* tps) {
   mfa_status st = mfa::validate_decode_desc(d, window, mqa_entry);
   if (st != MFA_OK) return st;
   if (tq < 1 || tq > mfa::kMaxQueryTokens || (int64_t)d->batch * tq > (int64_t)INT32_MAX)
     return MFA_ERR_SHAPE;
+  *tps = (tq % 2 == 0) ? 2 : 1;
   *vd = *d;
-  vd->batch = d->batch * tq;
+  vd->batch = d->batch * (tq / *tps);
   if (tq > 1 && mfa::plan_decode(vd, window, 1).path != mfa::DecodePath::kMqaShared)
     return MFA_ERR_SHAPE;
   return MFA_OK;
@@ -119,7 +123,8 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
                        int32_t window, void* workspace, size_t workspace_bytes,
                        mfa_stream_t stream, bool mqa_entry) {
   mfa_decode_desc vd;
-  mfa_status st = query_slot_desc(d0, tq, window, mqa_entry, &vd);
+  int32_t tps = 1;
+  mfa_status st = query_slot_desc(d0, tq, window, mqa_entry, &vd, &tps);
   if (st != MFA_OK) return st;
   const mfa_decode_desc* d = &vd;
   if (d->batch == 0) return MFA_OK;
@@ -133,13 +138,15 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
     cus = device_cu_count();
     if (cus <= 0) return MFA_ERR_LAUNCH;
   }
-  const mfa::DecodePlan pl = mfa::plan_decode(d, window, cus);
+  const mfa::DecodePlan pl = mfa::plan_decode(d, window, cus, tps);
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return MFA_ERR_WORKSPACE;
 
   mfa::DecodeParams p = make_params(d, pl, q, k_cache, v_cache, block_table, ctx_lens, k_scale,
                                     v_scale, out, scale, window, workspace);
   p.tq = tq;
+  p.tps = tps;
+  p.hq = d->num_q_heads * tps;   // query rows per slot
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   switch (pl.path) {
@@ -155,7 +162,7 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
   }
   if (e != hipSuccess) return MFA_ERR_LAUNCH;
   if (pl.splits > 1 && pl.path != mfa::DecodePath::kF32) {
-    e = mfa::launch_combine(p, pl.group, d->head_dim, s);
+    e = mfa::launch_combine(p, pl.group * tps, d->head_dim, s);
     if (e != hipSuccess) return MFA_ERR_LAUNCH;
   }
   return MFA_OK;
@@ -187,13 +194,14 @@ mfa_status mfa_decode_attention_mtp(const mfa_decode_desc* desc, int32_t num_que
 
 size_t mfa_decode_mtp_workspace_size(const mfa_decode_desc* desc, int32_t num_query_tokens) {
   mfa_decode_desc vd;
-  if (query_slot_desc(desc, num_query_tokens, 0, true, &vd) != MFA_OK) return 0;
+  int32_t tps = 1;
+  if (query_slot_desc(desc, num_query_tokens, 0, true, &vd, &tps) != MFA_OK) return 0;
   int cus = 0;
   if (vd.num_splits == 0) {
     cus = device_cu_count();
     if (cus <= 0) return 0;
   }
-  return mfa::plan_decode(&vd, 0, cus).workspace_bytes;
+  return mfa::plan_decode(&vd, 0, cus, tps).workspace_bytes;
 }
 
 mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
