@@ -153,6 +153,9 @@ def main():
                     help="each step appends one token per slot (mfa_kv_append, length "
                          "advanced on the device) before the attention; lengths start "
                          "steps+warmup below the workload's and grow to it")
+    ap.add_argument("--mtp", type=int, default=1,
+                    help="query tokens per slot (multi-token decode, causal among them; the "
+                         "contexts count them); dense one-KV-head configs only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -192,6 +195,15 @@ def main():
         pools.append((t["k"].clone(), t["v"].clone()))
     out = t["out"]
     window = case.window
+    tq = args.mtp
+    if tq != 1:
+        if case.hkv != 1 or window or args.with_append or tq < 1:
+            raise SystemExit("--mtp takes a dense one-KV-head config (2, 3 or 4), without "
+                             "--with-append")
+        from workloads import make_mtp_queries
+        qm = make_mtp_queries(606, batch=case.batch, tq=tq, hq=case.hq, d=case.d)
+        t["q"] = torch.from_numpy(qm.view(np.int16)).view(torch.bfloat16).to(dev)
+        out = torch.empty((case.batch, tq, case.hq, case.d), dtype=torch.bfloat16, device=dev)
     n_calls = max(args.warmup, len(pools)) + args.steps
     if args.with_append:
         # A decode loop: the device-side lengths start n_calls below the
@@ -213,7 +225,11 @@ def main():
         if args.with_append:
             mfa.mfa_kv_append(new_kv[0], new_kv[1], k, v, t["table"], t["lens"],
                               k_scale=t["k_scale"], v_scale=t["v_scale"])
-        if case.hkv == 1 and window == 0:
+        if tq != 1:
+            mfa.mfa_decode_attention_mtp(t["q"], k, v, t["table"], t["lens"], out, case.scale,
+                                         k_scale=t["k_scale"], v_scale=t["v_scale"],
+                                         num_splits=args.num_splits)
+        elif case.hkv == 1 and window == 0:
             mfa.mfa_decode_attention(t["q"], k, v, t["table"], t["lens"], out, case.scale,
                                      k_scale=t["k_scale"], v_scale=t["v_scale"],
                                      num_splits=args.num_splits)
@@ -272,18 +288,25 @@ def main():
         append_bytes = case.batch * (2 * case.hkv * case.d * (2 + elem) + 8)
         nbytes += append_bytes
     else:
-        nbytes = accounting.decode_call_bytes(case.ctx_lens, hq=case.hq, hkv=case.hkv, d=case.d,
-                                              q_fmt="bf16", kv_fmt=fmt_kv,
+        # Multi-token: each sequence's K/V once, and Tq rows of q and out.
+        nbytes = accounting.decode_call_bytes(case.ctx_lens, hq=case.hq * tq, hkv=case.hkv,
+                                              d=case.d, q_fmt="bf16", kv_fmt=fmt_kv,
                                               out_fmt=case.out_format, window=window)
-    flops = accounting.decode_call_flops(case.ctx_lens, hq=case.hq, d=case.d, window=window)
+    flops = sum(accounting.decode_call_flops(np.maximum(case.ctx_lens - (tq - 1 - j), 0),
+                                             hq=case.hq, d=case.d, window=window)
+                for j in range(tq))
     achieved = nbytes / (call_ms * 1e-3) / 1e9
-    desc = mfa.decode_desc(t["q"], t["k"], t["table"], out, args.num_splits)
+    # Split count of the query slots (a pair of tokens per slot for even Tq).
+    slots = case.batch * (tq // 2 if tq % 2 == 0 else tq)
+    desc = mfa.decode_desc(t["q"][:slots] if tq == 1 else t["q"].view(-1, case.hq, case.d)[:slots],
+                           t["k"], t["table"], out.view(-1, case.hq, case.d)[:slots],
+                           args.num_splits)
     splits = mfa.mfa_decode_plan_splits(desc, window,
                                         torch.cuda.get_device_properties(dev).multi_processor_count)
 
     res = {
         "metric": METRIC,
-        "value": case.batch / (ms_per_step * 1e-3),
+        "value": case.batch * tq / (ms_per_step * 1e-3),
         "unit": "query tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -301,7 +324,7 @@ def main():
                    "kv_heads": case.hkv, "head_dim": case.d, "kv_dtype": fmt_kv,
                    "page": 64, "window": window, "splits": splits, "kv_pool_copies": len(pools),
                    "launch": "hip graph replay" if args.graph else "eager",
-                   "append": bool(args.with_append)},
+                   "append": bool(args.with_append), "query_tokens_per_slot": tq},
         "hbm_gbps": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "call_us_mean": call_ms * 1e3,
@@ -309,7 +332,8 @@ def main():
         "append_bytes_per_call": append_bytes,
         "flops_per_call": flops,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(args.config),
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": committed_traffic(args.config) if tq == 1 else None,
                      "timed": "one HIP event pair around the timed steps on the launch "
                               "stream, divided by the step count (attention kernel + split "
                               "merge kernel per step" + (", after the KV append)" if
