@@ -25,6 +25,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn query tokens/s + achieved HBM GB/s (% peak), MFA 4K ctx, batch 64"
 HBM_PEAK_GBPS = 8000.0
+PAGE = 64
 
 
 def log(msg):
@@ -135,6 +136,66 @@ def copy_calibration(steps):
     print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": steps}), flush=True)
 
 
+def latency_model(steps, warmup):
+    """Fit the attention-FFN ratio page's attention latency model
+    t_A = alpha_A * T + beta_A to this library on one GPU: MFA decode calls
+    (64 heads, one 256-wide K/V head, paged) over uniform batches, B slots of
+    L keys each, T = B * L cached tokens; bf16 and FP8 caches.  Each call
+    reads blocks no other call of the sweep point reads (the pool is cycled
+    through), so the timings are HBM timings, not cache hits."""
+    import torch
+    import decode_attention_mfa_amd as mfa
+    from decode_attention_mfa_amd import accounting
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_blocks = 32768                                   # 2M tokens, 1 GiB per bf16 pool
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(707)
+    kb = torch.randn((n_blocks, 1, PAGE, 256), generator=gen, device=dev, dtype=torch.bfloat16)
+    vb = torch.randn((n_blocks, 1, 256, PAGE), generator=gen, device=dev, dtype=torch.bfloat16)
+    pools = {"bf16": (kb, vb, None),
+             "e4m3": (kb.to(torch.float8_e4m3fn), vb.to(torch.float8_e4m3fn),
+                      torch.ones(1, dtype=torch.float32, device=dev))}
+    perm = torch.from_numpy(np.random.default_rng(708).permutation(n_blocks).astype(np.int32)).to(dev)
+    fits = {}
+    for fmt, (k, v, sc) in pools.items():
+        pts = []
+        for B in (16, 32, 64, 128, 256):
+            for L in (1024, 2048, 4096, 8192):
+                nb = L // PAGE
+                need = B * nb
+                sets = max(1, n_blocks // need)
+                tables = [perm[j * need:(j + 1) * need].view(B, nb) for j in range(sets)]
+                lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+                q = torch.randn((B, 64, 256), generator=gen, device=dev, dtype=torch.bfloat16)
+                out = torch.empty_like(q)
+
+                def call(i):
+                    mfa.mfa_decode_attention(q, k, v, tables[i % sets], lens, out, 1.0 / 16,
+                                             k_scale=sc, v_scale=sc)
+                for i in range(warmup):
+                    call(i)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(steps):
+                    call(warmup + i)
+                e1.record()
+                torch.cuda.synchronize()
+                pts.append((B, L, B * L, e0.elapsed_time(e1) * 1e-3 / steps))
+                log(f"latency model {fmt}: B={B} L={L} {pts[-1][3] * 1e6:.1f} us")
+        alpha, beta, r2 = accounting.fit_latency_model([x[2] for x in pts], [x[3] for x in pts])
+        kv_bytes = 2 * 256 * accounting.DTYPE_BYTES[fmt]
+        fits[fmt] = {"alpha_A_ns_per_token": alpha * 1e9, "beta_A_us": beta * 1e6, "r2": r2,
+                     "kv_bytes_per_token": kv_bytes,
+                     "bandwidth_of_alpha_GBps": kv_bytes / alpha / 1e9,
+                     "points_B_L_us": [[b, l, round(t * 1e6, 2)] for b, l, _, t in pts]}
+    print(json.dumps({"latency_model": "t_A = alpha_A * T + beta_A (T = sum of context lengths)",
+                      "workload": "MFA decode, 64 q heads / 1 KV head, d=256, paged, uniform "
+                                  "lengths, B in {16..256}, L in {1K..8K}",
+                      "steps_per_point": steps, "fits": fits}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +217,9 @@ def main():
     ap.add_argument("--mtp", type=int, default=1,
                     help="query tokens per slot (multi-token decode, causal among them; the "
                          "contexts count them); dense one-KV-head configs only")
+    ap.add_argument("--latency-model", action="store_true",
+                    help="fit t_A = alpha_A * T + beta_A over a sweep of batch sizes and "
+                         "context lengths (bf16 and FP8 caches) and print the fits")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -165,6 +229,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.latency_model:
+        latency_model(min(args.steps, 30), min(args.warmup, 5))
         return
 
     import torch

@@ -95,3 +95,35 @@ def step5_cache_payload(T, *, global_layers=23, local_layers=69, window=512, hkv
     per_tok = kv_bytes_per_token(hkv, d, 2)
     return (per_tok * global_layers * T, per_tok * local_layers * window,
             global_layers * math.ceil(T / block) * summary_dim)
+
+
+# ---- attention latency model (attention-FFN ratio page) ----
+# The page models one attention step's latency as linear in the batch's token
+# load, t_A = alpha_A * T + beta_A (a roofline-based linear model, Section
+# "three-regime analysis"), where T is the number of cached tokens the step's
+# attention reads (sum of the slots' context lengths), and replaces the
+# drifting expected load by its horizon average, which tends to
+# T_bar = B * (mu_P + mu_D) with mu_D = (1 - p) / p for geometric decode
+# lengths (Proposition 4.3 as the page restates it).
+
+def horizon_token_load(batch, mu_p, p):
+    """Large-N horizon-average token load B (mu_P + (1 - p) / p)."""
+    return batch * (mu_p + (1.0 - p) / p)
+
+
+def fit_latency_model(token_loads, times):
+    """Least-squares line times = alpha * token_loads + beta.
+
+    Returns (alpha, beta, r2): seconds per cached token, fixed seconds per
+    step, and the coefficient of determination of the fit."""
+    import numpy as np
+    T = np.asarray(token_loads, dtype=np.float64)
+    t = np.asarray(times, dtype=np.float64)
+    if T.size < 2 or np.ptp(T) == 0:
+        raise ValueError("need at least two distinct token loads")
+    A = np.stack([T, np.ones_like(T)], axis=1)
+    (alpha, beta), *_ = np.linalg.lstsq(A, t, rcond=None)
+    resid = t - (alpha * T + beta)
+    ss_tot = float(np.sum((t - t.mean()) ** 2))
+    r2 = 1.0 - float(resid @ resid) / ss_tot if ss_tot > 0 else 1.0
+    return float(alpha), float(beta), r2
