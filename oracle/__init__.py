@@ -28,6 +28,11 @@ What it computes, and which passage each function follows:
 * :func:`decode_attention_mtp` -- several new query tokens per sequence (MTP
   drafts or a speculative verify, Step-3 report section 5.2), causal among
   themselves: token t of Tq attends the first L - (Tq - 1 - t) keys.
+* :mod:`oracle.sparse` -- Step-5 sparse global attention for a decode token
+  ("Step-5-Preview" page, indexer and attention sections): coordinatewise
+  block summaries, weighted-ReLU scores on E4M3-rounded operands, causal
+  top-512 selection with ties to the lower id plus the current block, and
+  softmax attention over the selected original K/V.
 * :mod:`oracle.codecs` -- bf16 and OCP FP8 E4M3 (E4M3FN) storage decoders.
 
 Pins (tests/test_oracle_*.py) tie every function to something other than

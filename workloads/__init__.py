@@ -14,6 +14,8 @@ from .gen import (
     make_decode_case,
     make_mtp_queries,
     make_query_inputs,
+    make_sparse_indexer_inputs,
+    SparseIndexerInputs,
     ragged_lengths,
     CONFIG_NAMES,
 )
@@ -27,6 +29,8 @@ __all__ = [
     "make_decode_case",
     "make_mtp_queries",
     "make_query_inputs",
+    "make_sparse_indexer_inputs",
+    "SparseIndexerInputs",
     "ragged_lengths",
     "CONFIG_NAMES",
 ]

@@ -236,6 +236,28 @@ def make_mtp_queries(seed, *, batch, tq, hq=64, d=256, q_format="bf16"):
     return _storage(rng.standard_normal((batch, tq, hq, d), dtype=np.float32), q_format)
 
 
+@dataclass
+class SparseIndexerInputs:
+    """Step-5 indexer inputs of a batch (raw storage): search queries
+    q_idx [B, 4, 4, 256] and proxy keys / compression logits k_idx, z
+    [B, cap, 256] as bf16 bits, search-head weights w [B, 4, 4] float32."""
+    q_idx: np.ndarray
+    w: np.ndarray
+    k_idx: np.ndarray
+    z: np.ndarray
+
+
+def make_sparse_indexer_inputs(seed, *, batch, cap, groups=4, heads=4, width=256):
+    """N(0, 1) search queries, proxy keys and logits (bf16); weights
+    N(0, 1) * 4^-1/2, the prescale the page says the weights carry."""
+    rng = np.random.default_rng(seed)
+    q_idx = bf16_round_bits(rng.standard_normal((batch, groups, heads, width), dtype=np.float32))
+    w = (rng.standard_normal((batch, groups, heads), dtype=np.float32) * np.float32(0.5))
+    k_idx = bf16_round_bits(rng.standard_normal((batch, cap, width), dtype=np.float32))
+    z = bf16_round_bits(rng.standard_normal((batch, cap, width), dtype=np.float32))
+    return SparseIndexerInputs(q_idx=q_idx, w=w, k_idx=k_idx, z=z)
+
+
 def ragged_lengths(batch, *, p_lo=1024, p_hi=8192, geo_p=1.0 / 1024, cap=32768):
     """Continuous-batching context lengths: prefill length ~ Uniform{p_lo..p_hi}
     plus a decode index ~ Geometric(p) on {0, 1, ...} (numpy counts trials from 1,
