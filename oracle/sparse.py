@@ -54,8 +54,9 @@ def block_summaries(k_idx, z, length):
     Returns (exact [nb, 256] float64, codes [nb, 256] uint8 E4M3 of the bf16-
     rounded summaries)."""
     nb = int(length) // BLOCK
-    k = np.asarray(k_idx, dtype=np.float64)[:nb * BLOCK].reshape(nb, BLOCK, -1)
-    zz = np.asarray(z, dtype=np.float64)[:nb * BLOCK].reshape(nb, BLOCK, -1)
+    width = np.shape(k_idx)[-1]
+    k = np.asarray(k_idx, dtype=np.float64)[:nb * BLOCK].reshape(nb, BLOCK, width)
+    zz = np.asarray(z, dtype=np.float64)[:nb * BLOCK].reshape(nb, BLOCK, width)
     e = np.exp(zz - zz.max(axis=1, keepdims=True))
     a = e / e.sum(axis=1, keepdims=True)          # softmax over the block, per coordinate
     c = (a * k).sum(axis=1)

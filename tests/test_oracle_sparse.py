@@ -43,8 +43,9 @@ def test_summary_closed_forms():
     c, codes = block_summaries(k, z, 16)
     assert np.allclose(c[0], k[win, np.arange(256)], rtol=0, atol=1e-12)
     assert np.allclose(c[1], k[8 + 7 - win, np.arange(256)], rtol=0, atol=1e-12)
-    # only complete blocks: 15 tokens make one summary
+    # only complete blocks: 15 tokens make one summary, 7 none
     assert block_summaries(k, z, 15)[0].shape == (1, 256)
+    assert block_summaries(k, z, 7)[0].shape == (0, 256)
     # storage: E4M3 of the bf16 rounding
     assert np.array_equal(e4m3fn_codes_to_f64(codes), e4m3_round(bf16_round(c)))
 
