@@ -11,6 +11,9 @@ from .binding import (
     mfa_decode_workspace_size,
     mfa_kv_append,
     mfa_query_proj,
+    mfa_sparse_attention,
+    mfa_sparse_select,
+    mfa_sparse_summarize,
 )
 
 __all__ = [
@@ -22,4 +25,7 @@ __all__ = [
     "mfa_decode_workspace_size",
     "mfa_kv_append",
     "mfa_query_proj",
+    "mfa_sparse_attention",
+    "mfa_sparse_select",
+    "mfa_sparse_summarize",
 ]

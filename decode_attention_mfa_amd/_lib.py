@@ -27,6 +27,10 @@ EXPORTED = (
     "mfa_kv_append",
     "mfa_query_proj",
     "mfa_query_proj_workspace_size",
+    "mfa_sparse_summarize",
+    "mfa_sparse_select",
+    "mfa_sparse_attention",
+    "mfa_sparse_workspace_size",
     "mfa_status_string",
     "mfa_abi_version",
 )
@@ -73,6 +77,16 @@ class MfaQueryProjDesc(ctypes.Structure):
     ]
 
 
+class MfaSparseDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("out_dtype", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
 _LIB = None
 
 
@@ -114,6 +128,16 @@ def load():
     lib.mfa_query_proj.restype = ctypes.c_int
     lib.mfa_query_proj_workspace_size.argtypes = [qp_p]
     lib.mfa_query_proj_workspace_size.restype = ctypes.c_size_t
+    sp_p = ctypes.POINTER(MfaSparseDesc)
+    lib.mfa_sparse_summarize.argtypes = [sp_p, P, P, P, P, P]
+    lib.mfa_sparse_summarize.restype = ctypes.c_int
+    lib.mfa_sparse_select.argtypes = [sp_p, P, P, P, P, P, P, P]
+    lib.mfa_sparse_select.restype = ctypes.c_int
+    lib.mfa_sparse_attention.argtypes = [sp_p, P, P, P, P, P, P, P, P, ctypes.c_float, P,
+                                         ctypes.c_size_t, P]
+    lib.mfa_sparse_attention.restype = ctypes.c_int
+    lib.mfa_sparse_workspace_size.argtypes = [sp_p]
+    lib.mfa_sparse_workspace_size.restype = ctypes.c_size_t
     lib.mfa_status_string.argtypes = [ctypes.c_int]
     lib.mfa_status_string.restype = ctypes.c_char_p
     lib.mfa_abi_version.argtypes = []

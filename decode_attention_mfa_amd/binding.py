@@ -17,7 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (MFA_BF16, MFA_F32, MFA_FP8_E4M3, MfaDecodeDesc, MfaKvAppendDesc,
-                   MfaQueryProjDesc, check)
+                   MfaQueryProjDesc, MfaSparseDesc, check)
 
 PAGE = 64
 _workspaces = {}
@@ -184,6 +184,48 @@ def mfa_kv_append(k_new, v_new, k_cache, v_cache, block_table, ctx_lens, *, k_sc
     check(lib.mfa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                             _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(k_scale),
                             _ptr(v_scale), _ptr(active), _stream(k_new, stream)))
+
+
+def sparse_desc(batch, block_table, k_cache, out, num_splits=0):
+    return MfaSparseDesc(batch=batch, max_blocks_per_seq=block_table.shape[1],
+                         num_blocks=k_cache.shape[0] if k_cache is not None else 0,
+                         out_dtype=_dtype_code(out) if out is not None else MFA_BF16,
+                         num_splits=int(num_splits))
+
+
+def mfa_sparse_summarize(k_idx, z, ctx_lens, summaries, *, block_table, stream=None):
+    """Block summaries of the complete 8-token blocks; see mfa_sparse_summarize."""
+    lib = _lib.load()
+    desc = sparse_desc(k_idx.shape[0], block_table, None, None)
+    check(lib.mfa_sparse_summarize(ctypes.byref(desc), _ptr(k_idx), _ptr(z), _ptr(ctx_lens),
+                                   _ptr(summaries), _stream(k_idx, stream)))
+    return summaries
+
+
+def mfa_sparse_select(q_idx, w, summaries, ctx_lens, selected, num_selected, *, block_table,
+                      stream=None):
+    """Weighted-ReLU scores and the causal top-512; see mfa_sparse_select."""
+    lib = _lib.load()
+    desc = sparse_desc(q_idx.shape[0], block_table, None, None)
+    check(lib.mfa_sparse_select(ctypes.byref(desc), _ptr(q_idx), _ptr(w), _ptr(summaries),
+                                _ptr(ctx_lens), _ptr(selected), _ptr(num_selected),
+                                _stream(q_idx, stream)))
+    return selected, num_selected
+
+
+def mfa_sparse_attention(q, k_cache, v_cache, block_table, ctx_lens, selected, num_selected, out,
+                         scale, *, num_splits=0, workspace=None, stream=None):
+    """Attention over the selected blocks and the current block; see
+    mfa_sparse_attention."""
+    lib = _lib.load()
+    desc = sparse_desc(q.shape[0], block_table, k_cache, out, num_splits)
+    need = int(lib.mfa_sparse_workspace_size(ctypes.byref(desc)))
+    ws, ws_bytes = _workspace(q.device, need, workspace, "sparse")
+    check(lib.mfa_sparse_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_table), _ptr(ctx_lens), _ptr(selected),
+                                   _ptr(num_selected), _ptr(out), ctypes.c_float(scale), _ptr(ws),
+                                   ctypes.c_size_t(ws_bytes), _stream(q, stream)))
+    return out
 
 
 def query_proj_desc(x, w_qup, q_out, num_heads, eps):

@@ -290,6 +290,73 @@ mfa_status mfa_query_proj(const mfa_query_proj_desc* desc, const void* x, const 
 
 size_t mfa_query_proj_workspace_size(const mfa_query_proj_desc* desc);
 
+/*
+ * Step-5 sparse global attention for one decode token per request
+ * ("Step-5-Preview: Sparse GQA, Indexer und KV-Speicher", the indexer and
+ * attention sections).  Shapes are the Step-5 layer's: 64 query heads in 4 KV
+ * groups of width 192 (bf16, paged like mfa_decode_attention_gqa), an indexer
+ * of 4 provider groups x 4 search heads x 256 proxy coordinates, 8-token
+ * blocks and 512 selected blocks.  The decode token of request b sits at
+ * t = L - 1, L = ctx_lens[b] (counting it).  Three calls:
+ *   mfa_sparse_summarize  block summaries c[r] of the complete blocks
+ *   mfa_sparse_select     weighted-ReLU scores and the causal top-512
+ *   mfa_sparse_attention  softmax attention over the selected original K/V
+ */
+typedef struct mfa_sparse_desc {
+  int32_t batch;               /* requests B                                     */
+  int32_t max_blocks_per_seq;  /* 64-token pages per request (<= 512: 32K tokens)*/
+  int64_t num_blocks;          /* blocks in the paged K/V pool                   */
+  int32_t out_dtype;           /* MFA_BF16 or MFA_F32                            */
+  int32_t num_splits;          /* 0 = heuristic, else forced (1..65)             */
+} mfa_sparse_desc;
+
+/*
+ * Summaries of every complete block r < floor(L / 8) of each request:
+ * c[r, d] = sum_j softmax_j(z[8r + j, d]) k_idx[8r + j, d] over the block's 8
+ * tokens, per coordinate d, in fp32, rounded to bf16 and stored as the
+ * nearest E4M3FN code (ties to even, saturating).
+ *   k_idx, z    [B, max_blocks_per_seq * 64, 256] bf16 proxy keys and
+ *               compression logits, token-major
+ *   summaries   [B, max_blocks_per_seq * 8, 256] uint8 E4M3 codes; entries of
+ *               incomplete or absent blocks are left as they are
+ */
+mfa_status mfa_sparse_summarize(const mfa_sparse_desc* desc, const void* k_idx, const void* z,
+                                const int32_t* ctx_lens, uint8_t* summaries, mfa_stream_t stream);
+
+/*
+ * Scores s[g, r] = sum_h w[g, h] ReLU(Q8(q_idx[g, h]) . c[r]) for the
+ * candidate blocks r < floor(t / 8), Q8 the E4M3 rounding (fp32 sums), and
+ * per group the 512 highest, equal scores to the lower block id.
+ *   q_idx          [B, 4, 4, 256] bf16 search queries
+ *   w              [B, 4, 4] fp32 signed search-head weights (prescale included)
+ *   summaries      as written by mfa_sparse_summarize
+ *   selected       [B, 4, 512] int32: the selected block ids, ascending
+ *   num_selected   [B, 4] int32: min(candidates, 512)
+ */
+mfa_status mfa_sparse_select(const mfa_sparse_desc* desc, const void* q_idx, const float* w,
+                             const uint8_t* summaries, const int32_t* ctx_lens, int32_t* selected,
+                             int32_t* num_selected, mfa_stream_t stream);
+
+/*
+ * out[b, h] = softmax attention of q[b, h] over J[t, g(h)]: the tokens of the
+ * selected blocks and of the current block up to t, g(h) = floor(h / 16).
+ *   q            [B, 64, 192] bf16
+ *   k_cache      [num_blocks, 4, 64, 192] bf16;  v_cache [num_blocks, 4, 192, 64]
+ *   block_table  [B, max_blocks_per_seq] int32
+ *   selected, num_selected   as written by mfa_sparse_select (ids outside the
+ *                candidates are clamped into them; counts into [0, 512])
+ *   out          [B, 64, 192] out_dtype; a request with L == 0 gets zeros
+ *   workspace    at least mfa_sparse_workspace_size(desc) bytes, 256-aligned
+ */
+mfa_status mfa_sparse_attention(const mfa_sparse_desc* desc, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table,
+                                const int32_t* ctx_lens, const int32_t* selected,
+                                const int32_t* num_selected, void* out, float scale,
+                                void* workspace, size_t workspace_bytes, mfa_stream_t stream);
+
+/* Workspace bytes of mfa_sparse_attention (0 for one split or a bad desc). */
+size_t mfa_sparse_workspace_size(const mfa_sparse_desc* desc);
+
 /* Static, never-NULL description of a status code. */
 const char* mfa_status_string(mfa_status status);
 

@@ -171,3 +171,33 @@ def test_multi_token_entry_rules():
         got = lib.mfa_decode_mtp_workspace_size(ctypes.byref(desc(num_splits=4)), tq)
         assert got == lib.mfa_decode_workspace_size(ctypes.byref(desc(batch=64 * tq, num_splits=4)), 0)
     assert lib.mfa_decode_mtp_workspace_size(ctypes.byref(desc()), 0) == 0
+
+
+def sparse(**kw):
+    from decode_attention_mfa_amd._lib import MfaSparseDesc
+    d = dict(batch=32, max_blocks_per_seq=512, num_blocks=16384, out_dtype=MFA_BF16, num_splits=0)
+    d.update(kw)
+    return MfaSparseDesc(**d)
+
+
+def test_sparse_entry_rules():
+    lib = _lib.load()
+    att = lambda d, ws=None, nbytes=0, q=A: lib.mfa_sparse_attention(
+        ctypes.byref(d) if d is not None else None, q, A, A, A, A, A, A, A, ctypes.c_float(0.07),
+        ws, ctypes.c_size_t(nbytes), None)
+    assert att(None) == MFA_ERR_NULL
+    assert att(sparse(out_dtype=MFA_FP8_E4M3)) == MFA_ERR_DTYPE
+    assert att(sparse(max_blocks_per_seq=513)) == MFA_ERR_SHAPE         # > 4096 candidate blocks
+    assert att(sparse(num_splits=66)) == MFA_ERR_SHAPE
+    assert att(sparse(num_blocks=0, num_splits=1)) == MFA_ERR_SHAPE
+    assert att(sparse(), q=None) == MFA_ERR_NULL
+    assert att(sparse(), q=ctypes.c_void_p(0x10008)) == MFA_ERR_ALIGN
+    assert att(sparse(num_splits=2)) == MFA_ERR_WORKSPACE
+    assert att(sparse(batch=0), q=None) == 0
+    assert lib.mfa_sparse_summarize(ctypes.byref(sparse()), None, A, A, A, None) == MFA_ERR_NULL
+    assert lib.mfa_sparse_select(ctypes.byref(sparse()), A, A, A, A, A, None, None) == MFA_ERR_NULL
+    # two splits of 33 tiles: partials of 32 x 4 groups x 16 heads x 2 splits
+    rows = 32 * 4 * 16 * 2
+    got = lib.mfa_sparse_workspace_size(ctypes.byref(sparse(num_splits=2)))
+    assert got >= rows * (192 * 4 + 8) and got % 256 == 0
+    assert lib.mfa_sparse_workspace_size(ctypes.byref(sparse(num_splits=1))) == 0
