@@ -136,6 +136,79 @@ def copy_calibration(steps):
     print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": steps}), flush=True)
 
 
+def sparse_step(steps, warmup, batch=32, ctx=32768):
+    """Time the Step-5 sparse global attention decode step on the global
+    layer's shape (B requests of ctx tokens, 64 q heads / 4 KV groups / 192,
+    bf16, paged): indexer scores + top-512 selection, then attention over the
+    selected blocks and the current block.  The block summaries are built
+    once beforehand (a decode step adds at most one per request) and timed
+    on their own."""
+    import torch
+    import decode_attention_mfa_amd as mfa
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pages = ctx // PAGE
+    n_blocks = batch * pages
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(909)
+    k = torch.randn((n_blocks, 4, PAGE, 192), generator=gen, device=dev, dtype=torch.bfloat16)
+    v = torch.randn((n_blocks, 4, PAGE // 8, 192, 8), generator=gen, device=dev, dtype=torch.bfloat16)
+    table = torch.from_numpy(np.random.default_rng(910).permutation(n_blocks).astype(np.int32)
+                             .reshape(batch, pages)).to(dev)
+    lens = torch.full((batch,), ctx, dtype=torch.int32, device=dev)
+    q = torch.randn((batch, 64, 192), generator=gen, device=dev, dtype=torch.bfloat16)
+    q_idx = torch.randn((batch, 4, 4, 256), generator=gen, device=dev, dtype=torch.bfloat16)
+    w = torch.randn((batch, 4, 4), generator=gen, device=dev) * 0.5
+    k_idx = torch.randn((batch, ctx, 256), generator=gen, device=dev, dtype=torch.bfloat16)
+    z = torch.randn((batch, ctx, 256), generator=gen, device=dev, dtype=torch.bfloat16)
+    summ = torch.zeros((batch, pages * 8, 256), dtype=torch.uint8, device=dev)
+    sel = torch.empty((batch, 4, 512), dtype=torch.int32, device=dev)
+    nsel = torch.empty((batch, 4), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    scale = 1.0 / np.sqrt(192)
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    t_sum = timed(lambda: mfa.mfa_sparse_summarize(k_idx, z, lens, summ, block_table=table), 5)
+    t_sel = timed(lambda: mfa.mfa_sparse_select(q_idx, w, summ, lens, sel, nsel,
+                                                block_table=table), steps)
+    t_att = timed(lambda: mfa.mfa_sparse_attention(q, k, v, table, lens, sel, nsel, out, scale),
+                  steps)
+
+    def step():
+        mfa.mfa_sparse_select(q_idx, w, summ, lens, sel, nsel, block_table=table)
+        mfa.mfa_sparse_attention(q, k, v, table, lens, sel, nsel, out, scale)
+    t_step = timed(step, steps)
+    cand = (ctx - 1) // 8
+    tokens = 512 * 8 + (ctx - 1) % 8 + 1                       # |J| per (request, group)
+    att_bytes = batch * (4 * tokens * 192 * 2 * 2 + 64 * 192 * 2 * 2)
+    sel_bytes = batch * (cand * 256 + 16 * 256 * 2 + 16 * 4 + 4 * 512 * 4)
+    nbytes = att_bytes + sel_bytes
+    print(json.dumps({
+        "metric": "Step-5 sparse global attention decode step (select + attention)",
+        "value": batch / t_step, "unit": "query tokens/s", "ms_per_step": t_step * 1e3,
+        "config": {"workload": f"Step-5 global sparse layer: B={batch}, context {ctx}, 64 q heads / "
+                               "4 KV groups / d=192 bf16, indexer 4x4x256, 8-token blocks, top-512",
+                   "batch": batch, "ctx": ctx},
+        "select_us": t_sel * 1e6, "attention_us": t_att * 1e6,
+        "summaries_all_blocks_us": t_sum * 1e6,
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": nbytes / t_step / 1e9, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": nbytes / t_step / 1e9 / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "dense_kv_bytes_per_step": batch * 4 * ctx * 192 * 2 * 2}), flush=True)
+
+
 def latency_model(steps, warmup):
     """Fit the attention-FFN ratio page's attention latency model
     t_A = alpha_A * T + beta_A to this library on one GPU: MFA decode calls
@@ -220,6 +293,9 @@ def main():
     ap.add_argument("--latency-model", action="store_true",
                     help="fit t_A = alpha_A * T + beta_A over a sweep of batch sizes and "
                          "context lengths (bf16 and FP8 caches) and print the fits")
+    ap.add_argument("--sparse", action="store_true",
+                    help="time the Step-5 sparse global attention decode step (B=32, 32K "
+                         "context) and print its own line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -229,6 +305,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.sparse:
+        sparse_step(min(args.steps, 50), min(args.warmup, 5))
         return
     if args.latency_model:
         latency_model(min(args.steps, 30), min(args.warmup, 5))

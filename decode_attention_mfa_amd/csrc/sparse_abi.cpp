@@ -145,9 +145,10 @@ mfa_status mfa_sparse_attention(const mfa_sparse_desc* desc, const void* q, cons
   dp.k_block_stride = (int64_t)kHkv * 64 * kD;
   dp.k_head_stride = (int64_t)64 * kD;
   dp.k_row_stride = kD;
+  // V^T in 8-token sub-blocks: [num_blocks, 4, 8, 192, 8].
   dp.v_block_stride = (int64_t)kHkv * kD * 64;
   dp.v_head_stride = (int64_t)kD * 64;
-  dp.v_row_stride = 64;
+  dp.v_row_stride = 8;
   p.sel = selected;
   p.nsel = num_selected;
   return mfa::launch_sparse_attention(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess

@@ -25,8 +25,11 @@
 // tiles through an LDS ring filled by 16-byte global->LDS copies, wave w
 // takes keys 16w .. 16w+15 of every tile, the four waves merged through LDS)
 // with a gathered tile: tile i holds list entries 8i .. 8i+7, each an 8-token
-// block (8 consecutive rows of a 64-token page, 16 bytes of every V^T row), so
-// every copy still moves 16 contiguous bytes.
+// block.  Its K is 8 consecutive rows of a 64-token page (3 KB); its V^T is
+// one contiguous [192][8] sub-block, because this layer's V cache is stored
+// channel-major per 8-token sub-block ([blocks, 4, 8, 192, 8]) rather than
+// per page: a selected block then costs two 3 KB reads, where a page-wide
+// V^T row would give 16 isolated bytes per channel.
 #include "device_common.h"
 #include "fp8_encode.h"
 #include "sparse_params.h"
@@ -108,7 +111,7 @@ __global__ void __launch_bounds__(256) sparse_summary_kernel(SparseParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. Scores and top-512: one workgroup of 4 waves per request.
+// 2. Scores and top-512: one workgroup of 8 waves per (request, group).
 
 // Order-preserving 32-bit image of a float (larger float -> larger integer).
 __device__ __forceinline__ uint32_t mono_bits(float s) {
@@ -120,8 +123,10 @@ __device__ __forceinline__ uint64_t select_key(float s, int r) {
   return ((uint64_t)mono_bits(s) << 12) | (uint64_t)(kSparseMaxCand - 1 - r);
 }
 
-// Inclusive prefix sum of one value per thread over the 256 threads.
-__device__ __forceinline__ int block_scan_incl(int v, int* wsum) {
+constexpr int kSelThreads = 512;   // 8 waves per (request, group)
+
+// Inclusive prefix sum of one value per thread over the workgroup.
+__device__ __forceinline__ int sel_scan_incl(int v, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -132,26 +137,33 @@ __device__ __forceinline__ int block_scan_incl(int v, int* wsum) {
   __syncthreads();
   int pre = 0;
 #pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) pre += (w2 < wave) ? wsum[w2] : 0;
+  for (int w2 = 0; w2 < kSelThreads / 64; ++w2) pre += (w2 < wave) ? wsum[w2] : 0;
   __syncthreads();
   return v + pre;
 }
 
-__global__ void __launch_bounds__(256) sparse_select_kernel(SparseParams p) {
-  __shared__ float sc[kSparseGroups][kSparseMaxCand];   // 64 KB
+// One workgroup per (request, group).  The score tiles of 16 candidates are
+// taken 8 per wave at a time, all their summary loads issued before the
+// first product (the loop is otherwise bound by load latency).
+__global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams p) {
+  constexpr int kWaves = kSelThreads / 64;
+  constexpr int kUnroll = 8;
+  __shared__ float sc[kSparseMaxCand];   // 16 KB
   __shared__ int hist[256];
-  __shared__ int wsum[4];
+  __shared__ int wsum[kWaves];
   __shared__ int pick[2];
 
-  const int b = blockIdx.x;
+  const int bg = blockIdx.x;
+  const int b = bg / kSparseGroups, g = bg - b * kSparseGroups;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = slot_len(p.dp.ctx_lens[b], p.dp.max_blocks);
   const int t = L - 1;
   const int R = t >= 0 ? min(t / kSparseBlock, p.cap8) : 0;   // candidate blocks
 
-  // Q8 fragments: column col = 4g + h of lane l % 16; K-step c takes
-  // coordinates 64(c/2) + 16(l/16) + 8(c%2) .. +7, the channel map under
-  // which one 16-byte read of codes holds two steps' A operands.
+  // Q8 fragments: column col = 4g' + h of lane l % 16 (all four groups; this
+  // workgroup keeps group g); K-step c takes coordinates
+  // 64(c/2) + 16(l/16) + 8(c%2) .. +7, the channel map under which one
+  // 16-byte read of codes holds two steps' A operands.
   const int col = lane & 15, q4 = lane >> 4;
   const int grp = col >> 2, sh = col & 3;
   intx4 qf[kSparseWidth / 32];
@@ -176,78 +188,83 @@ __global__ void __launch_bounds__(256) sparse_select_kernel(SparseParams p) {
   }
   const float wgt = p.w[(b * kSparseGroups + grp) * kSparseHeads + sh];
 
-  // Scores of 16 candidates per tile; wave w takes tiles w, w + 4, ...
-  const uint8_t* cb = p.summ + (int64_t)b * p.cap8 * kSparseWidth;
-  for (int tile = wave; 16 * tile < R; tile += 4) {
-    const int row = min(16 * tile + col, R - 1);
-    const uint8_t* cr = cb + (int64_t)row * kSparseWidth + 16 * q4;
-    floatx4 st = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t* cb = p.summ + (int64_t)b * p.cap8 * kSparseWidth + 16 * q4;
+  for (int t0 = wave * kUnroll; 16 * t0 < R; t0 += kWaves * kUnroll) {
+    intx4 raw[kUnroll][kSparseWidth / 64];
 #pragma unroll
-    for (int u = 0; u < kSparseWidth / 64; ++u) {
-      const intx4 raw = *reinterpret_cast<const intx4*>(cr + 64 * u);
-      st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw.x, raw.y), qf[2 * u], st);
-      st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw.z, raw.w), qf[2 * u + 1], st);
+    for (int k = 0; k < kUnroll; ++k) {
+      const int row = min(16 * (t0 + k) + col, R - 1);
+#pragma unroll
+      for (int u = 0; u < kSparseWidth / 64; ++u)
+        raw[k][u] = *reinterpret_cast<const intx4*>(cb + (int64_t)row * kSparseWidth + 64 * u);
     }
-    // Lane (col, q4) holds candidates 16 tile + 4 q4 + i for column col.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = wgt * fmaxf(st[i], 0.f);
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      const int cand = 16 * tile + 4 * q4 + i;
-      if (sh == 0 && cand < R) sc[grp][cand] = v + 0.f;   // -0 -> +0: equal scores compare equal
+    for (int k = 0; k < kUnroll; ++k) {
+      floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kSparseWidth / 64; ++u) {
+        st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[k][u].x, raw[k][u].y), qf[2 * u], st);
+        st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[k][u].z, raw[k][u].w), qf[2 * u + 1], st);
+      }
+      // Lane (col, q4) holds candidates 16 tile + 4 q4 + i for column col.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = wgt * fmaxf(st[i], 0.f);
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        const int cand = 16 * (t0 + k) + 4 * q4 + i;
+        if (grp == g && sh == 0 && cand < R) sc[cand] = v + 0.f;   // -0 -> +0: equal scores compare equal
+      }
     }
   }
   __syncthreads();
 
-  for (int g = 0; g < kSparseGroups; ++g) {
-    int32_t* out = p.sel_out + (int64_t)(b * kSparseGroups + g) * kSparseBudget;
-    if (R <= kSparseBudget) {
-      for (int r = tid; r < R; r += 256) out[r] = r;
-      if (tid == 0) p.nsel_out[b * kSparseGroups + g] = R;
-      continue;
-    }
-    // Radix select of the 512th largest key, most significant digit first.
-    uint64_t prefix = 0, mask = 0;
-    int need = kSparseBudget;
-    for (int pass = 0; pass < 6; ++pass) {
-      const int shift = 40 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-      for (int r = tid; r < R; r += 256) {
-        const uint64_t key = select_key(sc[g][r], r);
-        if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255)], 1);
-      }
-      __syncthreads();
-      // Thread i looks at digit 255 - i: counts of higher digits before it.
-      const int cnt = hist[255 - tid];
-      const int incl = block_scan_incl(cnt, wsum);
-      if (incl >= need && incl - cnt < need) {
-        pick[0] = 255 - tid;
-        pick[1] = need - (incl - cnt);
-      }
-      __syncthreads();
-      prefix |= (uint64_t)pick[0] << shift;
-      mask |= (uint64_t)255 << shift;
-      need = pick[1];
-      __syncthreads();
-    }
-    // Keys at or above the 512th: exactly 512; written in ascending id order.
-    constexpr int kPer = kSparseMaxCand / 256;
-    int mine = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int r = tid * kPer + k;
-      mine += (r < R && select_key(sc[g][r], r) >= prefix) ? 1 : 0;
-    }
-    int pos = block_scan_incl(mine, wsum) - mine;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int r = tid * kPer + k;
-      if (r < R && select_key(sc[g][r], r) >= prefix) out[pos++] = r;
-    }
-    if (tid == 0) p.nsel_out[b * kSparseGroups + g] = kSparseBudget;
+  int32_t* out = p.sel_out + (int64_t)bg * kSparseBudget;
+  if (R <= kSparseBudget) {
+    for (int r = tid; r < R; r += kSelThreads) out[r] = r;
+    if (tid == 0) p.nsel_out[bg] = R;
+    return;
   }
+  // Radix select of the 512th largest key, most significant digit first.
+  uint64_t prefix = 0, mask = 0;
+  int need = kSparseBudget;
+  for (int pass = 0; pass < 6; ++pass) {
+    const int shift = 40 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int r = tid; r < R; r += kSelThreads) {
+      const uint64_t key = select_key(sc[r], r);
+      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255)], 1);
+    }
+    __syncthreads();
+    // Thread i < 256 looks at digit 255 - i: counts of higher digits before it.
+    const int cnt = tid < 256 ? hist[255 - tid] : 0;
+    const int incl = sel_scan_incl(cnt, wsum);
+    if (tid < 256 && incl >= need && incl - cnt < need) {
+      pick[0] = 255 - tid;
+      pick[1] = need - (incl - cnt);
+    }
+    __syncthreads();
+    prefix |= (uint64_t)pick[0] << shift;
+    mask |= (uint64_t)255 << shift;
+    need = pick[1];
+    __syncthreads();
+  }
+  // Keys at or above the 512th: exactly 512; written in ascending id order.
+  constexpr int kPer = kSparseMaxCand / kSelThreads;
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int r = tid * kPer + k;
+    mine += (r < R && select_key(sc[r], r) >= prefix) ? 1 : 0;
+  }
+  int pos = sel_scan_incl(mine, wsum) - mine;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int r = tid * kPer + k;
+    if (r < R && select_key(sc[r], r) >= prefix) out[pos++] = r;
+  }
+  if (tid == 0) p.nsel_out[bg] = kSparseBudget;
 }
 
 // ---------------------------------------------------------------------------
@@ -356,14 +373,16 @@ __global__ void __launch_bounds__(256) sparse_attention_kernel(SparseParams sp) 
               dst + i * 1024);
       }
     } else {
-      // V^T tile: chunk c of row (channel) ch holds entry e0 + c's 8 keys.
+      // V^T tile: chunk c of row (channel) ch holds entry e0 + c's 8 keys,
+      // the 16 bytes of channel ch in that block's [192][8] V^T sub-block.
 #pragma unroll
       for (int k = 0; k < kDmaPerWave; ++k) {
         const int i = wave * kDmaPerWave + k;
         const int row = 8 * i + (lane >> 3);
         const int c = (lane & 7) ^ swz_v(row);
         const int e = e0 + c;
-        dma16(vpool + (int64_t)ent_blk[e] * p.v_block_stride + row * p.v_row_stride + ent_row[e],
+        dma16(vpool + (int64_t)ent_blk[e] * p.v_block_stride + (ent_row[e] >> 3) * (kD * kSparseBlock) +
+                  row * kSparseBlock,
               dst + i * 1024);
       }
     }
@@ -510,7 +529,8 @@ hipError_t launch_sparse_summary(const SparseParams& p, hipStream_t stream) {
 
 hipError_t launch_sparse_select(const SparseParams& p, hipStream_t stream) {
   if (p.cap8 > kSparseMaxCand) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sparse_select_kernel, dim3((unsigned)p.dp.batch), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(sparse_select_kernel, dim3((unsigned)(p.dp.batch * kSparseGroups)), dim3(kSelThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

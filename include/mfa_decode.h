@@ -341,7 +341,10 @@ mfa_status mfa_sparse_select(const mfa_sparse_desc* desc, const void* q_idx, con
  * out[b, h] = softmax attention of q[b, h] over J[t, g(h)]: the tokens of the
  * selected blocks and of the current block up to t, g(h) = floor(h / 16).
  *   q            [B, 64, 192] bf16
- *   k_cache      [num_blocks, 4, 64, 192] bf16;  v_cache [num_blocks, 4, 192, 64]
+ *   k_cache      [num_blocks, 4, 64, 192] bf16 (as the GQA entry)
+ *   v_cache      [num_blocks, 4, 8, 192, 8] bf16: V^T per 8-token sub-block
+ *                (token j of a block: sub-block (j % 64) / 8, column j % 8),
+ *                so a selected block's V is one contiguous 3 KB read
  *   block_table  [B, max_blocks_per_seq] int32
  *   selected, num_selected   as written by mfa_sparse_select (ids outside the
  *                candidates are clamped into them; counts into [0, 512])

@@ -96,8 +96,10 @@ def attended_tokens(selected, t):
 def sparse_attention(q, k_cache, v_cache, block_table, b, t, selected, scale, *,
                      q_format="bf16", kv_format="bf16"):
     """Attention of request b's decode token (position t) over J[t, g] for
-    every head.  q [Hq, d] raw; paged caches as decode_attention; selected is
-    the per-group list of block ids.  Returns float64 [Hq, d]."""
+    every head.  q [Hq, d] raw; K paged as decode_attention, V^T stored per
+    8-token sub-block, [blocks, Hkv, P/8, d, 8] (token j of a page in
+    sub-block j // 8, column j % 8); selected is the per-group list of block
+    ids.  Returns float64 [Hq, d]."""
     q = np.asarray(q)
     hq, d = q.shape
     hkv = k_cache.shape[1]
@@ -112,7 +114,7 @@ def sparse_attention(q, k_cache, v_cache, block_table, b, t, selected, scale, *,
         blocks = np.asarray(block_table[b], dtype=np.int64)[J // page]
         rows = J % page
         kc = k_cache[blocks, g, rows, :][None, :, None, :]                 # [1, n, 1, d]
-        vc = np.transpose(v_cache[blocks, g, :, rows], (1, 0))[None, None, :, :]   # [1, 1, d, n]
+        vc = np.transpose(v_cache[blocks, g, rows // BLOCK, :, rows % BLOCK], (1, 0))[None, None]   # [1, 1, d, n]
         qg = q[group * g:group * (g + 1)][None]
         out[group * g:group * (g + 1)] = decode_attention(
             qg, kc, vc, np.array([n]), scale, q_format=q_format, kv_format=kv_format)[0]

@@ -14,7 +14,7 @@ import decode_attention_mfa_amd as mfa
 from oracle.codecs import bf16_bits_to_f64, e4m3fn_codes_to_f64
 from oracle.sparse import (block_summaries, indexer_scores, select_blocks, sparse_attention,
                            sparse_decode)
-from workloads import make_decode_case, make_sparse_indexer_inputs
+from workloads import make_decode_case, make_sparse_indexer_inputs, v_by_subblock
 
 from gpu_helpers import _raw_to_tensor, assert_parity
 
@@ -131,12 +131,13 @@ def test_attention_over_the_oracle_selection(splits):
             nsel[b, g] = len(ref[g])
     q = _raw_to_tensor(case.q, "bf16", "cuda")
     k = _raw_to_tensor(case.k_cache, "bf16", "cuda")
-    v = _raw_to_tensor(case.v_cache, "bf16", "cuda")
+    vs = v_by_subblock(case.v_cache)                    # this layer's V layout
+    v = _raw_to_tensor(vs, "bf16", "cuda")
     out = torch.full((case.batch, 64, 192), float("nan"), dtype=torch.bfloat16, device="cuda")
     mfa.mfa_sparse_attention(q, k, v, d["table"], d["lens"], torch.from_numpy(sel).cuda(),
                              torch.from_numpy(nsel).cuda(), out, case.scale, num_splits=splits)
     torch.cuda.synchronize()
-    ref = np.stack([sparse_attention(case.q[b], case.k_cache, case.v_cache, case.block_table, b,
+    ref = np.stack([sparse_attention(case.q[b], case.k_cache, vs, case.block_table, b,
                                      int(L) - 1, refsel[b][1], case.scale)
                     for b, L in enumerate(case.ctx_lens)])
     assert_parity(out, ref, "bf16", f"sparse attention splits={splits}")
@@ -152,7 +153,8 @@ def test_whole_step_end_to_end():
     d = _dev(case, idx, np.zeros((case.batch, case.max_blocks * 8, 256), np.uint8))
     q = _raw_to_tensor(case.q, "bf16", "cuda")
     k = _raw_to_tensor(case.k_cache, "bf16", "cuda")
-    v = _raw_to_tensor(case.v_cache, "bf16", "cuda")
+    vs = v_by_subblock(case.v_cache)                    # this layer's V layout
+    v = _raw_to_tensor(vs, "bf16", "cuda")
     out = torch.empty((case.batch, 64, 192), dtype=torch.bfloat16, device="cuda")
     mfa.mfa_sparse_summarize(d["k_idx"], d["z"], d["lens"], d["summ"], block_table=d["table"])
     mfa.mfa_sparse_select(d["q_idx"], d["w"], d["summ"], d["lens"], d["sel"], d["nsel"],
@@ -161,7 +163,7 @@ def test_whole_step_end_to_end():
     torch.cuda.synchronize()
     summ = _host_summaries(case, idx)
     assert np.array_equal(d["summ"].cpu().numpy(), summ)
-    ref, refsel = sparse_decode(case.q, idx.q_idx, idx.w, summ, case.k_cache, case.v_cache,
+    ref, refsel = sparse_decode(case.q, idx.q_idx, idx.w, summ, case.k_cache, vs,
                                 case.block_table, case.ctx_lens, case.scale)
     gsel, gn = d["sel"].cpu().numpy(), d["nsel"].cpu().numpy()
     for b in range(case.batch):

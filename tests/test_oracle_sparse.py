@@ -16,7 +16,7 @@ from oracle import decode_attention
 from oracle.codecs import bf16_bits_to_f64, e4m3fn_codes_to_f64
 from oracle.sparse import (attended_tokens, block_summaries, bf16_round, e4m3_round,
                            indexer_scores, select_blocks, sparse_attention)
-from workloads import make_decode_case
+from workloads import make_decode_case, v_by_subblock
 
 
 def test_roundings_match_torch_casts():
@@ -103,7 +103,7 @@ def test_all_blocks_selected_is_dense_attention():
     case = _gqa_case(L)
     t = L - 1
     sel = [np.arange(t // 8)] * 4
-    got = sparse_attention(case.q[0], case.k_cache, case.v_cache, case.block_table, 0, t, sel,
+    got = sparse_attention(case.q[0], case.k_cache, v_by_subblock(case.v_cache), case.block_table, 0, t, sel,
                            case.scale)
     ref = decode_attention(case.q, case.k_cache, case.v_cache, [L], case.scale, q_format="bf16",
                            kv_format="bf16", block_table=case.block_table)[0]
@@ -116,7 +116,7 @@ def test_subset_matches_brute_force_softmax():
     t = L - 1
     rng = np.random.default_rng(5)
     sel = [np.sort(rng.choice(t // 8, size=512, replace=False)) for _ in range(4)]
-    got = sparse_attention(case.q[0], case.k_cache, case.v_cache, case.block_table, 0, t, sel,
+    got = sparse_attention(case.q[0], case.k_cache, v_by_subblock(case.v_cache), case.block_table, 0, t, sel,
                            case.scale)
     for h in (0, 17, 40, 63):
         g = h // 16

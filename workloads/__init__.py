@@ -17,6 +17,7 @@ from .gen import (
     make_sparse_indexer_inputs,
     SparseIndexerInputs,
     ragged_lengths,
+    v_by_subblock,
     CONFIG_NAMES,
 )
 
@@ -32,5 +33,6 @@ __all__ = [
     "make_sparse_indexer_inputs",
     "SparseIndexerInputs",
     "ragged_lengths",
+    "v_by_subblock",
     "CONFIG_NAMES",
 ]

@@ -247,6 +247,14 @@ class SparseIndexerInputs:
     z: np.ndarray
 
 
+def v_by_subblock(v_cache, block=8):
+    """A paged V^T cache [blocks, Hkv, d, P] relaid per sub-block of `block`
+    tokens: [blocks, Hkv, P / block, d, block] (data movement only)."""
+    nb, hkv, d, page = v_cache.shape
+    return np.ascontiguousarray(
+        v_cache.reshape(nb, hkv, d, page // block, block).transpose(0, 1, 3, 2, 4))
+
+
 def make_sparse_indexer_inputs(seed, *, batch, cap, groups=4, heads=4, width=256):
     """N(0, 1) search queries, proxy keys and logits (bf16); weights
     N(0, 1) * 4^-1/2, the prescale the page says the weights carry."""
