@@ -131,7 +131,7 @@ def load():
     sp_p = ctypes.POINTER(MfaSparseDesc)
     lib.mfa_sparse_summarize.argtypes = [sp_p, P, P, P, P, P]
     lib.mfa_sparse_summarize.restype = ctypes.c_int
-    lib.mfa_sparse_select.argtypes = [sp_p, P, P, P, P, P, P, P]
+    lib.mfa_sparse_select.argtypes = [sp_p, P, P, P, P, P, P, ctypes.c_void_p, ctypes.c_size_t, P]
     lib.mfa_sparse_select.restype = ctypes.c_int
     lib.mfa_sparse_attention.argtypes = [sp_p, P, P, P, P, P, P, P, P, ctypes.c_float, P,
                                          ctypes.c_size_t, P]

@@ -203,13 +203,15 @@ def mfa_sparse_summarize(k_idx, z, ctx_lens, summaries, *, block_table, stream=N
 
 
 def mfa_sparse_select(q_idx, w, summaries, ctx_lens, selected, num_selected, *, block_table,
-                      stream=None):
+                      workspace=None, stream=None):
     """Weighted-ReLU scores and the causal top-512; see mfa_sparse_select."""
     lib = _lib.load()
     desc = sparse_desc(q_idx.shape[0], block_table, None, None)
+    need = int(lib.mfa_sparse_workspace_size(ctypes.byref(desc)))
+    ws, ws_bytes = _workspace(q_idx.device, need, workspace, "sparse")
     check(lib.mfa_sparse_select(ctypes.byref(desc), _ptr(q_idx), _ptr(w), _ptr(summaries),
-                                _ptr(ctx_lens), _ptr(selected), _ptr(num_selected),
-                                _stream(q_idx, stream)))
+                                _ptr(ctx_lens), _ptr(selected), _ptr(num_selected), _ptr(ws),
+                                ctypes.c_size_t(ws_bytes), _stream(q_idx, stream)))
     return selected, num_selected
 
 

@@ -46,7 +46,9 @@ int32_t plan_splits(const mfa_sparse_desc* d) {
 
 struct Plan {
   int32_t splits, chunk;
-  size_t part_o, part_ml, bytes;
+  size_t part_o, part_ml;
+  size_t attn_bytes;   // the attention's split partials
+  size_t bytes;        // the workspace: partials or the selection's scores
 };
 
 Plan plan(const mfa_sparse_desc* d) {
@@ -57,8 +59,12 @@ Plan plan(const mfa_sparse_desc* d) {
     const size_t rows = (size_t)d->batch * kHkv * pl.splits * 16;
     pl.part_o = 0;
     pl.part_ml = align_up(rows * kD * sizeof(float), kAlign);
-    pl.bytes = align_up(pl.part_ml + rows * 2 * sizeof(float), kAlign);
+    pl.attn_bytes = align_up(pl.part_ml + rows * 2 * sizeof(float), kAlign);
   }
+  // The selection's scores [B, 4, cap8] fp32 share the workspace.
+  const size_t score_bytes =
+      align_up((size_t)d->batch * kHkv * d->max_blocks_per_seq * 8 * sizeof(float), kAlign);
+  pl.bytes = std::max(pl.attn_bytes, score_bytes);
   return pl;
 }
 
@@ -96,12 +102,17 @@ mfa_status mfa_sparse_summarize(const mfa_sparse_desc* desc, const void* k_idx, 
 
 mfa_status mfa_sparse_select(const mfa_sparse_desc* desc, const void* q_idx, const float* w,
                              const uint8_t* summaries, const int32_t* ctx_lens, int32_t* selected,
-                             int32_t* num_selected, mfa_stream_t stream) {
+                             int32_t* num_selected, void* workspace, size_t workspace_bytes,
+                             mfa_stream_t stream) {
   const mfa_status st = validate(desc);
   if (st != MFA_OK || desc->batch == 0) return st;
   if (!q_idx || !w || !summaries || !ctx_lens || !selected || !num_selected) return MFA_ERR_NULL;
   if (!aligned16(q_idx) || !aligned16(summaries)) return MFA_ERR_ALIGN;
+  const Plan pl = plan(desc);
+  if (!workspace || workspace_bytes < pl.bytes) return MFA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return MFA_ERR_ALIGN;
   mfa::SparseParams p = base_params(desc, ctx_lens);
+  p.scores = static_cast<float*>(workspace);
   p.q_idx = q_idx;
   p.w = w;
   p.summ = summaries;
@@ -125,7 +136,7 @@ mfa_status mfa_sparse_attention(const mfa_sparse_desc* desc, const void* q, cons
   if (!std::isfinite(scale)) return MFA_ERR_ARG;
   if (desc->num_blocks <= 0) return MFA_ERR_SHAPE;
   const Plan pl = plan(desc);
-  if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return MFA_ERR_WORKSPACE;
+  if (pl.attn_bytes > 0 && (!workspace || workspace_bytes < pl.attn_bytes)) return MFA_ERR_WORKSPACE;
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kAlign)) return MFA_ERR_ALIGN;
   mfa::SparseParams p = base_params(desc, ctx_lens);
   mfa::DecodeParams& dp = p.dp;

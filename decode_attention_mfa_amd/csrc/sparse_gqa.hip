@@ -4,11 +4,11 @@
 //      c[r, d] = sum_j softmax_j(z[8r + j, d]) kI[8r + j, d], one coordinate
 //      per thread, fp32, rounded to bf16 and stored as E4M3 (section "Acht
 //      Tokens ergeben einen Such-Key - koordinatenweise").
-//   2. sparse_select_kernel: for the token at t = L - 1 and every provider
+//   2. sparse_score_kernel: for the token at t = L - 1 and every provider
 //      group g, s[g, r] = sum_h w[g, h] ReLU(Q8(qI[g, h]) . c[r]) over the
-//      candidate blocks r < floor(t / 8), then the 512 highest (equal scores
-//      to the lower block id), listed in ascending id order (section
-//      "Auswahl per gewichtetem ReLU-Score").
+//      candidate blocks r < floor(t / 8); sparse_select_kernel: the 512
+//      highest (equal scores to the lower block id), listed in ascending id
+//      order (section "Auswahl per gewichtetem ReLU-Score").
 //   3. sparse_attention_kernel: the 16 heads of group g attend the selected
 //      blocks' original K/V plus the current block up to t (section "Die
 //      eigentliche Attention liest weiterhin originale K/V").
@@ -16,10 +16,11 @@
 // The scores are one matrix product per request: S^T[block, (g, h)] =
 // C[block, :] . Q8^T, with the 16 columns exactly the 4 groups x 4 search
 // heads, on the 16x16x32 bf16 MFMA (E4M3 codes widen to bf16 exactly; the
-// products are exact, the sums fp32).  The top-512 is a radix select on a
-// 44-bit key (order-preserving score bits, then 4095 - id, so every key is
-// distinct and equal scores rank the lower id first), six 8-bit passes over
-// the scores kept in LDS, then an ordered compaction.
+// products are exact, the sums fp32).  The top-512 is a radix select on the
+// key (order-preserving score bits less those of the smallest score, then
+// 4095 - id, so every key is distinct and equal scores rank the lower id
+// first), in 8-bit passes over the scores kept in LDS, then an ordered
+// compaction.
 //
 // The attention kernel is the GQA decode kernel's pipeline (4 waves, 64-key
 // tiles through an LDS ring filled by 16-byte global->LDS copies, wave w
@@ -111,19 +112,16 @@ __global__ void __launch_bounds__(256) sparse_summary_kernel(SparseParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. Scores and top-512: one workgroup of 8 waves per (request, group).
+// 2. Scores, then the top-512.
 
 // Order-preserving 32-bit image of a float (larger float -> larger integer).
 __device__ __forceinline__ uint32_t mono_bits(float s) {
   const uint32_t u = __builtin_bit_cast(uint32_t, s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-// Selection key: score first, then the lower block id.
-__device__ __forceinline__ uint64_t select_key(float s, int r) {
-  return ((uint64_t)mono_bits(s) << 12) | (uint64_t)(kSparseMaxCand - 1 - r);
-}
 
 constexpr int kSelThreads = 512;   // 8 waves per (request, group)
+constexpr int kScoreChunk = 512;   // candidates per scoring workgroup
 
 // Inclusive prefix sum of one value per thread over the workgroup.
 __device__ __forceinline__ int sel_scan_incl(int v, int* wsum) {
@@ -142,28 +140,22 @@ __device__ __forceinline__ int sel_scan_incl(int v, int* wsum) {
   return v + pre;
 }
 
-// One workgroup per (request, group).  The score tiles of 16 candidates are
-// taken 8 per wave at a time, all their summary loads issued before the
-// first product (the loop is otherwise bound by load latency).
-__global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams p) {
-  constexpr int kWaves = kSelThreads / 64;
+// 2a. Scores: one workgroup of 4 waves per (request, 512 candidates), each
+// wave 8 tiles of 16 candidates with all summary loads issued before the
+// first product; scores[b, g, r] (fp32) go to the workspace.
+__global__ void __launch_bounds__(256) sparse_score_kernel(SparseParams p) {
   constexpr int kUnroll = 8;
-  __shared__ float sc[kSparseMaxCand];   // 16 KB
-  __shared__ int hist[256];
-  __shared__ int wsum[kWaves];
-  __shared__ int pick[2];
-
-  const int bg = blockIdx.x;
-  const int b = bg / kSparseGroups, g = bg - b * kSparseGroups;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = slot_len(p.dp.ctx_lens[b], p.dp.max_blocks);
   const int t = L - 1;
   const int R = t >= 0 ? min(t / kSparseBlock, p.cap8) : 0;   // candidate blocks
+  const int t0 = (blockIdx.x * kScoreChunk) / 16 + wave * kUnroll;   // first tile of this wave
+  if (R <= kSparseBudget || 16 * t0 >= R) return;   // every candidate is selected / none here
 
-  // Q8 fragments: column col = 4g' + h of lane l % 16 (all four groups; this
-  // workgroup keeps group g); K-step c takes coordinates
-  // 64(c/2) + 16(l/16) + 8(c%2) .. +7, the channel map under which one
-  // 16-byte read of codes holds two steps' A operands.
+  // Q8 fragments: column col = 4g + h of lane l % 16; K-step c takes
+  // coordinates 64(c/2) + 16(l/16) + 8(c%2) .. +7, the channel map under
+  // which one 16-byte read of codes holds two steps' A operands.
   const int col = lane & 15, q4 = lane >> 4;
   const int grp = col >> 2, sh = col & 3;
   intx4 qf[kSparseWidth / 32];
@@ -189,35 +181,50 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
   const float wgt = p.w[(b * kSparseGroups + grp) * kSparseHeads + sh];
 
   const uint8_t* cb = p.summ + (int64_t)b * p.cap8 * kSparseWidth + 16 * q4;
-  for (int t0 = wave * kUnroll; 16 * t0 < R; t0 += kWaves * kUnroll) {
-    intx4 raw[kUnroll][kSparseWidth / 64];
+  intx4 raw[kUnroll][kSparseWidth / 64];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int row = min(16 * (t0 + k) + col, R - 1);
+  for (int k = 0; k < kUnroll; ++k) {
+    const int row = min(16 * (t0 + k) + col, R - 1);
 #pragma unroll
-      for (int u = 0; u < kSparseWidth / 64; ++u)
-        raw[k][u] = *reinterpret_cast<const intx4*>(cb + (int64_t)row * kSparseWidth + 64 * u);
+    for (int u = 0; u < kSparseWidth / 64; ++u)
+      raw[k][u] = *reinterpret_cast<const intx4*>(cb + (int64_t)row * kSparseWidth + 64 * u);
+  }
+  float* scb = p.scores + (int64_t)(b * kSparseGroups + grp) * p.cap8;
+#pragma unroll
+  for (int k = 0; k < kUnroll; ++k) {
+    floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kSparseWidth / 64; ++u) {
+      st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[k][u].x, raw[k][u].y), qf[2 * u], st);
+      st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[k][u].z, raw[k][u].w), qf[2 * u + 1], st);
     }
+    // Lane (col, q4) holds candidates 16 tile + 4 q4 + i for column col;
+    // the sum over the group's four search heads is over lanes col ^ 1, ^ 2.
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      floatx4 st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < kSparseWidth / 64; ++u) {
-        st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[k][u].x, raw[k][u].y), qf[2 * u], st);
-        st = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[k][u].z, raw[k][u].w), qf[2 * u + 1], st);
-      }
-      // Lane (col, q4) holds candidates 16 tile + 4 q4 + i for column col.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = wgt * fmaxf(st[i], 0.f);
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        const int cand = 16 * (t0 + k) + 4 * q4 + i;
-        if (grp == g && sh == 0 && cand < R) sc[cand] = v + 0.f;   // -0 -> +0: equal scores compare equal
-      }
+    for (int i = 0; i < 4; ++i) {
+      float v = wgt * fmaxf(st[i], 0.f);
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      const int cand = 16 * (t0 + k) + 4 * q4 + i;
+      if (sh == 0 && cand < R) scb[cand] = v + 0.f;   // -0 -> +0: equal scores compare equal
     }
   }
-  __syncthreads();
+}
+
+// 2b. Top-512: one workgroup of 8 waves per (request, group) over the scores.
+__global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams p) {
+  constexpr int kWaves = kSelThreads / 64;
+  __shared__ float sc[kSparseMaxCand];   // 16 KB
+  __shared__ int hist[256];
+  __shared__ int wsum[kWaves];
+  __shared__ int pick[2];
+
+  const int bg = blockIdx.x;
+  const int b = bg / kSparseGroups;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = slot_len(p.dp.ctx_lens[b], p.dp.max_blocks);
+  const int t = L - 1;
+  const int R = t >= 0 ? min(t / kSparseBlock, p.cap8) : 0;   // candidate blocks
 
   int32_t* out = p.sel_out + (int64_t)bg * kSparseBudget;
   if (R <= kSparseBudget) {
@@ -225,15 +232,52 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
     if (tid == 0) p.nsel_out[bg] = R;
     return;
   }
+  const float* scg = p.scores + (int64_t)bg * p.cap8;
+  for (int r = tid; r < R; r += kSelThreads) sc[r] = scg[r];
+  __syncthreads();
+
+  // Keys relative to the smallest score: key = (mono(s) - mono(min)) << 12 |
+  // (4095 - id) keeps the order and drops the leading bits all scores share
+  // (sign, exponent), so the first radix digit already spreads the keys
+  // and only as many 8-bit passes run as the spread needs.
+  uint32_t lo_m = 0xFFFFFFFFu, hi_m = 0;
+  for (int r = tid; r < R; r += kSelThreads) {
+    const uint32_t m = mono_bits(sc[r]);
+    lo_m = min(lo_m, m);
+    hi_m = max(hi_m, m);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo_m = min(lo_m, (uint32_t)__shfl_xor((int)lo_m, off));
+    hi_m = max(hi_m, (uint32_t)__shfl_xor((int)hi_m, off));
+  }
+  if (lane == 0) {
+    wsum[wave] = (int)lo_m;
+    hist[wave] = (int)hi_m;
+  }
+  __syncthreads();
+  lo_m = 0xFFFFFFFFu;
+  hi_m = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    lo_m = min(lo_m, (uint32_t)wsum[w2]);
+    hi_m = max(hi_m, (uint32_t)hist[w2]);
+  }
+  __syncthreads();
+  const int bits = 12 + (hi_m > lo_m ? 32 - __builtin_clz(hi_m - lo_m) : 0);
+  const int passes = (bits + 7) / 8;
+  auto rel_key = [&](int r) {
+    return ((uint64_t)(mono_bits(sc[r]) - lo_m) << 12) | (uint64_t)(kSparseMaxCand - 1 - r);
+  };
   // Radix select of the 512th largest key, most significant digit first.
   uint64_t prefix = 0, mask = 0;
   int need = kSparseBudget;
-  for (int pass = 0; pass < 6; ++pass) {
-    const int shift = 40 - 8 * pass;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = 8 * (passes - 1 - pass);
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int r = tid; r < R; r += kSelThreads) {
-      const uint64_t key = select_key(sc[r], r);
+      const uint64_t key = rel_key(r);
       if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255)], 1);
     }
     __syncthreads();
@@ -256,13 +300,13 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int r = tid * kPer + k;
-    mine += (r < R && select_key(sc[r], r) >= prefix) ? 1 : 0;
+    mine += (r < R && rel_key(r) >= prefix) ? 1 : 0;
   }
   int pos = sel_scan_incl(mine, wsum) - mine;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int r = tid * kPer + k;
-    if (r < R && select_key(sc[r], r) >= prefix) out[pos++] = r;
+    if (r < R && rel_key(r) >= prefix) out[pos++] = r;
   }
   if (tid == 0) p.nsel_out[bg] = kSparseBudget;
 }
@@ -528,7 +572,9 @@ hipError_t launch_sparse_summary(const SparseParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_sparse_select(const SparseParams& p, hipStream_t stream) {
-  if (p.cap8 > kSparseMaxCand) return hipErrorInvalidValue;
+  if (p.cap8 > kSparseMaxCand || !p.scores) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sparse_score_kernel, dim3((unsigned)((p.cap8 + kScoreChunk - 1) / kScoreChunk), (unsigned)p.dp.batch),
+                     dim3(256), 0, stream, p);
   hipLaunchKernelGGL(sparse_select_kernel, dim3((unsigned)(p.dp.batch * kSparseGroups)), dim3(kSelThreads), 0,
                      stream, p);
   return hipGetLastError();

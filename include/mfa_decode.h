@@ -332,10 +332,14 @@ mfa_status mfa_sparse_summarize(const mfa_sparse_desc* desc, const void* k_idx, 
  *   summaries      as written by mfa_sparse_summarize
  *   selected       [B, 4, 512] int32: the selected block ids, ascending
  *   num_selected   [B, 4] int32: min(candidates, 512)
+ *   workspace      at least mfa_sparse_workspace_size(desc) bytes, 256-byte
+ *                  aligned (the fp32 scores); the same workspace serves
+ *                  mfa_sparse_attention when both are ordered on one stream
  */
 mfa_status mfa_sparse_select(const mfa_sparse_desc* desc, const void* q_idx, const float* w,
                              const uint8_t* summaries, const int32_t* ctx_lens, int32_t* selected,
-                             int32_t* num_selected, mfa_stream_t stream);
+                             int32_t* num_selected, void* workspace, size_t workspace_bytes,
+                             mfa_stream_t stream);
 
 /*
  * out[b, h] = softmax attention of q[b, h] over J[t, g(h)]: the tokens of the
@@ -357,7 +361,8 @@ mfa_status mfa_sparse_attention(const mfa_sparse_desc* desc, const void* q, cons
                                 const int32_t* num_selected, void* out, float scale,
                                 void* workspace, size_t workspace_bytes, mfa_stream_t stream);
 
-/* Workspace bytes of mfa_sparse_attention (0 for one split or a bad desc). */
+/* Workspace bytes of mfa_sparse_select and mfa_sparse_attention (the larger
+ * of the scores and the attention's split partials; 0 for a bad desc). */
 size_t mfa_sparse_workspace_size(const mfa_sparse_desc* desc);
 
 /* Static, never-NULL description of a status code. */

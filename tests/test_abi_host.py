@@ -195,9 +195,11 @@ def test_sparse_entry_rules():
     assert att(sparse(num_splits=2)) == MFA_ERR_WORKSPACE
     assert att(sparse(batch=0), q=None) == 0
     assert lib.mfa_sparse_summarize(ctypes.byref(sparse()), None, A, A, A, None) == MFA_ERR_NULL
-    assert lib.mfa_sparse_select(ctypes.byref(sparse()), A, A, A, A, A, None, None) == MFA_ERR_NULL
+    assert lib.mfa_sparse_select(ctypes.byref(sparse()), A, A, A, A, A, None, None, 0, None) == MFA_ERR_NULL
+    assert lib.mfa_sparse_select(ctypes.byref(sparse()), A, A, A, A, A, A, None, 0, None) == MFA_ERR_WORKSPACE
     # two splits of 33 tiles: partials of 32 x 4 groups x 16 heads x 2 splits
     rows = 32 * 4 * 16 * 2
     got = lib.mfa_sparse_workspace_size(ctypes.byref(sparse(num_splits=2)))
     assert got >= rows * (192 * 4 + 8) and got % 256 == 0
-    assert lib.mfa_sparse_workspace_size(ctypes.byref(sparse(num_splits=1))) == 0
+    # one split: the selection's fp32 scores [32, 4, 4096]
+    assert lib.mfa_sparse_workspace_size(ctypes.byref(sparse(num_splits=1))) == 32 * 4 * 4096 * 4
