@@ -421,6 +421,26 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     call_ms = start.elapsed_time(end) / args.steps
 
+    # The attention kernel alone (the roofline's kernel): a second pass of
+    # the same K steps launched in their two phases, a HIP event pair on the
+    # launch stream around each attention launch (the merge runs after it).
+    kernel_ms = None
+    if tq == 1 and case.hkv == 1 and window == 0 and not args.graph and not args.with_append:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            k, v = pools[i % len(pools)]
+            kw = dict(k_scale=t["k_scale"], v_scale=t["v_scale"], num_splits=args.num_splits)
+            pairs[i][0].record(stream)
+            mfa.mfa_decode_attention_phase(t["q"], k, v, t["table"], t["lens"], out, case.scale, 1,
+                                           **kw)
+            pairs[i][1].record(stream)
+            mfa.mfa_decode_attention_phase(t["q"], k, v, t["table"], t["lens"], out, case.scale, 2,
+                                           **kw)
+        torch.cuda.synchronize()
+        kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
     fmt_kv = case.kv_format
     append_bytes = 0
     if args.with_append:
@@ -442,6 +462,7 @@ def main():
                                              hq=case.hq, d=case.d, window=window)
                 for j in range(tq))
     achieved = nbytes / (call_ms * 1e-3) / 1e9
+    kernel_achieved = nbytes / (kernel_ms * 1e-3) / 1e9 if kernel_ms else None
     # Split count of the query slots (a pair of tokens per slot for even Tq).
     slots = case.batch * (tq // 2 if tq % 2 == 0 else tq)
     desc = mfa.decode_desc(t["q"][:slots] if tq == 1 else t["q"].view(-1, case.hq, case.d)[:slots],
@@ -477,13 +498,20 @@ def main():
         "algorithmic_bytes_per_call": nbytes,
         "append_bytes_per_call": append_bytes,
         "flops_per_call": flops,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": kernel_achieved or achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": (kernel_achieved or achieved) / HBM_PEAK_GBPS,
+                     "kernel_us": kernel_ms * 1e3 if kernel_ms else None,
+                     "step_achieved": achieved, "step_frac": achieved / HBM_PEAK_GBPS,
                      "traffic": committed_traffic(args.config) if tq == 1 else None,
-                     "timed": "one HIP event pair around the timed steps on the launch "
+                     "timed": ("the attention kernel: a HIP event pair on the launch stream "
+                               "around each of its K launches, in a second pass of the K steps "
+                               "launched in two phases; step_*: one event pair around the timed "
+                               "steps (attention + merge)") if kernel_ms else (
+                              "one HIP event pair around the timed steps on the launch "
                               "stream, divided by the step count (attention kernel + split "
                               "merge kernel per step" + (", after the KV append)" if
-                                                        args.with_append else ")")},
+                                                        args.with_append else ")"))},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample of the same workload")

@@ -21,6 +21,7 @@ EXPORTED = (
     "mfa_decode_attention",
     "mfa_decode_attention_gqa",
     "mfa_decode_attention_mtp",
+    "mfa_decode_attention_phase",
     "mfa_decode_workspace_size",
     "mfa_decode_mtp_workspace_size",
     "mfa_decode_plan_splits",
@@ -113,6 +114,9 @@ def load():
     lib.mfa_decode_attention_gqa.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float,
                                              ctypes.c_int32, P, ctypes.c_size_t, P]
     lib.mfa_decode_attention_gqa.restype = ctypes.c_int
+    lib.mfa_decode_attention_phase.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float, P,
+                                               ctypes.c_size_t, ctypes.c_int32, P]
+    lib.mfa_decode_attention_phase.restype = ctypes.c_int
     lib.mfa_decode_attention_mtp.argtypes = [desc_p, ctypes.c_int32, P, P, P, P, P, P, P, P,
                                              ctypes.c_float, P, ctypes.c_size_t, P]
     lib.mfa_decode_attention_mtp.restype = ctypes.c_int

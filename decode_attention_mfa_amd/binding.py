@@ -124,6 +124,22 @@ def mfa_decode_attention(q, k_cache, v_cache, block_table, ctx_lens, out, scale,
                    v_scale, 0, num_splits, workspace, stream)
 
 
+def mfa_decode_attention_phase(q, k_cache, v_cache, block_table, ctx_lens, out, scale, phase, *,
+                               k_scale=None, v_scale=None, num_splits=0, workspace=None,
+                               stream=None):
+    """One of the two launches of mfa_decode_attention (1: attention, 2: merge);
+    see mfa_decode_attention_phase in the header."""
+    lib = _lib.load()
+    _, desc_ref, need = _plan(q, k_cache, block_table, out, num_splits, 0)
+    ws, ws_bytes = _workspace(q.device, need, workspace, "decode")
+    check(lib.mfa_decode_attention_phase(desc_ref, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(block_table), _ptr(ctx_lens), _ptr(k_scale),
+                                         _ptr(v_scale), _ptr(out), ctypes.c_float(scale), _ptr(ws),
+                                         ctypes.c_size_t(ws_bytes), ctypes.c_int32(int(phase)),
+                                         _stream(q, stream)))
+    return out
+
+
 def mfa_decode_attention_gqa(q, k_cache, v_cache, block_table, ctx_lens, out, scale, *,
                              window=0, k_scale=None, v_scale=None, num_splits=0, workspace=None,
                              stream=None):

@@ -117,11 +117,12 @@ mfa_status query_slot_desc(const mfa_decode_desc* d, int32_t tq, int32_t window,
   return MFA_OK;
 }
 
+// phase: 0 = the whole call, 1 = the attention kernel only, 2 = the merge only.
 mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
                        const float* k_scale, const float* v_scale, void* out, float scale,
                        int32_t window, void* workspace, size_t workspace_bytes,
-                       mfa_stream_t stream, bool mqa_entry) {
+                       mfa_stream_t stream, bool mqa_entry, int phase = 0) {
   mfa_decode_desc vd;
   int32_t tps = 1;
   mfa_status st = query_slot_desc(d0, tq, window, mqa_entry, &vd, &tps);
@@ -149,7 +150,7 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
   p.hq = d->num_q_heads * tps;   // query rows per slot
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  switch (pl.path) {
+  if (phase != 2) switch (pl.path) {
     case mfa::DecodePath::kMqaShared:
       e = mfa::launch_mqa(p, d->kv_dtype == MFA_FP8_E4M3, s);
       break;
@@ -161,7 +162,7 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
       break;
   }
   if (e != hipSuccess) return MFA_ERR_LAUNCH;
-  if (pl.splits > 1 && pl.path != mfa::DecodePath::kF32) {
+  if (phase != 1 && pl.splits > 1 && pl.path != mfa::DecodePath::kF32) {
     e = mfa::launch_combine(p, pl.group * tps, d->head_dim, s);
     if (e != hipSuccess) return MFA_ERR_LAUNCH;
   }
@@ -179,6 +180,17 @@ mfa_status mfa_decode_attention(const mfa_decode_desc* desc, const void* q, cons
                                 size_t workspace_bytes, mfa_stream_t stream) {
   return decode_impl(desc, 1, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
                      scale, 0, workspace, workspace_bytes, stream, /*mqa_entry=*/true);
+}
+
+mfa_status mfa_decode_attention_phase(const mfa_decode_desc* desc, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      const float* k_scale, const float* v_scale, void* out,
+                                      float scale, void* workspace, size_t workspace_bytes,
+                                      int32_t phase, mfa_stream_t stream) {
+  if (phase != 1 && phase != 2) return MFA_ERR_ARG;
+  return decode_impl(desc, 1, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
+                     scale, 0, workspace, workspace_bytes, stream, /*mqa_entry=*/true, phase);
 }
 
 mfa_status mfa_decode_attention_mtp(const mfa_decode_desc* desc, int32_t num_query_tokens,

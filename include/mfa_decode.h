@@ -150,6 +150,22 @@ mfa_status mfa_decode_attention(const mfa_decode_desc* desc, const void* q,
                                 mfa_stream_t stream);
 
 /*
+ * mfa_decode_attention in its two launches, for callers that place work
+ * between them or time them apart: phase 1 enqueues the attention kernel
+ * (the split partials go to the workspace; with one split it writes out),
+ * phase 2 enqueues the merge of those partials into out (nothing with one
+ * split).  Arguments as mfa_decode_attention, identical for both phases and
+ * the same device; phase 2 must follow phase 1 on the stream with the
+ * workspace untouched in between.  Other phase values return MFA_ERR_ARG.
+ */
+mfa_status mfa_decode_attention_phase(const mfa_decode_desc* desc, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      const float* k_scale, const float* v_scale, void* out,
+                                      float scale, void* workspace, size_t workspace_bytes,
+                                      int32_t phase, mfa_stream_t stream);
+
+/*
  * Multi-token queries per slot (MTP / speculative verification, "Step-3 is
  * Large yet Affordable", section 5.2: MTP raises the attention's arithmetic
  * intensity).  Each cached sequence b has num_query_tokens = Tq new query

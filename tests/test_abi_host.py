@@ -203,3 +203,16 @@ def test_sparse_entry_rules():
     assert got >= rows * (192 * 4 + 8) and got % 256 == 0
     # one split: the selection's fp32 scores [32, 4, 4096]
     assert lib.mfa_sparse_workspace_size(ctypes.byref(sparse(num_splits=1))) == 32 * 4 * 4096 * 4
+
+
+def test_phase_entry_rules():
+    lib = _lib.load()
+    for phase in (0, 3, -1):
+        assert lib.mfa_decode_attention_phase(ctypes.byref(desc()), A, A, A, A, A, None, None, A,
+                                              ctypes.c_float(0.0625), None, ctypes.c_size_t(0),
+                                              ctypes.c_int32(phase), None) == MFA_ERR_ARG
+    # forced splits need the workspace in either phase
+    for phase in (1, 2):
+        assert lib.mfa_decode_attention_phase(ctypes.byref(desc()), A, A, A, A, A, None, None, A,
+                                              ctypes.c_float(0.0625), None, ctypes.c_size_t(0),
+                                              ctypes.c_int32(phase), None) == MFA_ERR_WORKSPACE

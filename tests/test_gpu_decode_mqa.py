@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+import decode_attention_mfa_amd as mfa
+
 from oracle import decode_attention
 from workloads import bf16_round_bits, config_case, make_decode_case
 
@@ -166,3 +168,21 @@ def test_balanced_partition_uniform_lengths(length):
     assert_parity(got, oracle(case), "bf16", f"uniform {length}")
     again = run_decode(case, t, num_splits=0)
     assert torch.equal(got.view(torch.int16), again.view(torch.int16))
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_two_phases_equal_the_whole_call(splits):
+    # mfa_decode_attention_phase 1 (attention) then 2 (merge) is the same
+    # computation as mfa_decode_attention: bit-identical outputs.
+    case = make_decode_case(331, batch=6, ctx_lens=[1, 64, 700, 4096, 0, 2049], hq=64, hkv=1,
+                            d=256, scale=1 / 16)
+    t = to_device(case)
+    whole = torch.full_like(t["out"], float("nan"))
+    mfa.mfa_decode_attention(t["q"], t["k"], t["v"], t["table"], t["lens"], whole, case.scale,
+                             num_splits=splits)
+    phased = torch.full_like(t["out"], float("nan"))
+    for phase in (1, 2):
+        mfa.mfa_decode_attention_phase(t["q"], t["k"], t["v"], t["table"], t["lens"], phased,
+                                       case.scale, phase, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), phased.view(torch.int16))
