@@ -19,7 +19,7 @@
 // products are exact, the sums fp32).  The top-512 is a radix select on the
 // key (order-preserving score bits less those of the smallest score, then
 // 4095 - id, so every key is distinct and equal scores rank the lower id
-// first), in 8-bit passes over the scores kept in LDS, then an ordered
+// first), in 11-bit passes over the scores kept in LDS, then an ordered
 // compaction.
 //
 // The attention kernel is the GQA decode kernel's pipeline (4 waves, 64-key
@@ -121,7 +121,7 @@ __device__ __forceinline__ uint32_t mono_bits(float s) {
 }
 
 constexpr int kSelThreads = 512;   // 8 waves per (request, group)
-constexpr int kScoreChunk = 512;   // candidates per scoring workgroup
+constexpr int kScoreChunk = 256;   // candidates per scoring workgroup
 
 // Inclusive prefix sum of one value per thread over the workgroup.
 __device__ __forceinline__ int sel_scan_incl(int v, int* wsum) {
@@ -140,45 +140,49 @@ __device__ __forceinline__ int sel_scan_incl(int v, int* wsum) {
   return v + pre;
 }
 
-// 2a. Scores: one workgroup of 4 waves per (request, 512 candidates), each
-// wave 8 tiles of 16 candidates with all summary loads issued before the
+// 2a. Scores: one workgroup of 4 waves per (request, 256 candidates), each
+// wave 4 tiles of 16 candidates with all summary loads issued before the
 // first product; scores[b, g, r] (fp32) go to the workspace.
 __global__ void __launch_bounds__(256) sparse_score_kernel(SparseParams p) {
-  constexpr int kUnroll = 8;
+  constexpr int kUnroll = kScoreChunk / 16 / 4;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = slot_len(p.dp.ctx_lens[b], p.dp.max_blocks);
   const int t = L - 1;
   const int R = t >= 0 ? min(t / kSparseBlock, p.cap8) : 0;   // candidate blocks
   const int t0 = (blockIdx.x * kScoreChunk) / 16 + wave * kUnroll;   // first tile of this wave
-  if (R <= kSparseBudget || 16 * t0 >= R) return;   // every candidate is selected / none here
+  if (R <= kSparseBudget || 16 * (blockIdx.x * kScoreChunk / 16) >= R) return;   // all selected / no candidate here
 
-  // Q8 fragments: column col = 4g + h of lane l % 16; K-step c takes
+  // Q8 of the request's 16 search queries, once per workgroup: thread t
+  // rounds values 16t .. 16t+15 to E4M3 and widens them back to bf16 (exact)
+  // into LDS.  Fragments: column col = 4g + h of lane l % 16; K-step c takes
   // coordinates 64(c/2) + 16(l/16) + 8(c%2) .. +7, the channel map under
   // which one 16-byte read of codes holds two steps' A operands.
+  __shared__ __attribute__((aligned(16))) uint16_t q8s[kSparseGroups * kSparseHeads * kSparseWidth];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q_idx) +
+                         (int64_t)b * kSparseGroups * kSparseHeads * kSparseWidth + 16 * threadIdx.x;
+    const intx4 v0 = *reinterpret_cast<const intx4*>(qp), v1 = *reinterpret_cast<const intx4*>(qp + 8);
+    const int w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    int codes[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      codes[k] = (int)((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)(w[2 * k] & 0xFFFF))) |
+                       ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)((uint32_t)w[2 * k] >> 16))) << 8) |
+                       ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)(w[2 * k + 1] & 0xFFFF)))) << 16 |
+                       ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)((uint32_t)w[2 * k + 1] >> 16))) << 24));
+    *reinterpret_cast<intx4*>(q8s + 16 * threadIdx.x) = e4m3x8_to_bf16(codes[0], codes[1]);
+    *reinterpret_cast<intx4*>(q8s + 16 * threadIdx.x + 8) = e4m3x8_to_bf16(codes[2], codes[3]);
+  }
+  __syncthreads();
   const int col = lane & 15, q4 = lane >> 4;
   const int grp = col >> 2, sh = col & 3;
   intx4 qf[kSparseWidth / 32];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q_idx) +
-                         ((int64_t)(b * kSparseGroups + grp) * kSparseHeads + sh) * kSparseWidth;
 #pragma unroll
-    for (int c = 0; c < kSparseWidth / 32; ++c) {
-      const intx4 raw = *reinterpret_cast<const intx4*>(qp + 64 * (c >> 1) + 16 * q4 + 8 * (c & 1));
-      // Q8: each bf16 value to its E4M3 code, then back to bf16 (exact).
-      uint32_t codes[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int wa = k ? raw.z : raw.x, wb = k ? raw.w : raw.y;
-        codes[k] = (uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)(wa & 0xFFFF))) |
-                   ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)((uint32_t)wa >> 16))) << 8) |
-                   ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)(wb & 0xFFFF)))) << 16 |
-                   ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)((uint32_t)wb >> 16))) << 24);
-      }
-      qf[c] = e4m3x8_to_bf16((int)codes[0], (int)codes[1]);
-    }
-  }
+  for (int c = 0; c < kSparseWidth / 32; ++c)
+    qf[c] = *reinterpret_cast<const intx4*>(q8s + col * kSparseWidth + 64 * (c >> 1) + 16 * q4 + 8 * (c & 1));
   const float wgt = p.w[(b * kSparseGroups + grp) * kSparseHeads + sh];
+  if (16 * t0 >= R) return;   // this wave's tiles are past the candidates
 
   const uint8_t* cb = p.summ + (int64_t)b * p.cap8 * kSparseWidth + 16 * q4;
   intx4 raw[kUnroll][kSparseWidth / 64];
@@ -214,8 +218,10 @@ __global__ void __launch_bounds__(256) sparse_score_kernel(SparseParams p) {
 // 2b. Top-512: one workgroup of 8 waves per (request, group) over the scores.
 __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams p) {
   constexpr int kWaves = kSelThreads / 64;
+  constexpr int kDigitBits = 11, kBins = 1 << kDigitBits;   // 4 bins per thread
+  static_assert(kBins == 4 * kSelThreads, "radix bins");
   __shared__ float sc[kSparseMaxCand];   // 16 KB
-  __shared__ int hist[256];
+  __shared__ int hist[kBins];
   __shared__ int wsum[kWaves];
   __shared__ int pick[2];
 
@@ -239,7 +245,7 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
   // Keys relative to the smallest score: key = (mono(s) - mono(min)) << 12 |
   // (4095 - id) keeps the order and drops the leading bits all scores share
   // (sign, exponent), so the first radix digit already spreads the keys
-  // and only as many 8-bit passes run as the spread needs.
+  // and only as many radix passes run as the spread needs.
   uint32_t lo_m = 0xFFFFFFFFu, hi_m = 0;
   for (int r = tid; r < R; r += kSelThreads) {
     const uint32_t m = mono_bits(sc[r]);
@@ -265,32 +271,41 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
   }
   __syncthreads();
   const int bits = 12 + (hi_m > lo_m ? 32 - __builtin_clz(hi_m - lo_m) : 0);
-  const int passes = (bits + 7) / 8;
   auto rel_key = [&](int r) {
     return ((uint64_t)(mono_bits(sc[r]) - lo_m) << 12) | (uint64_t)(kSparseMaxCand - 1 - r);
   };
-  // Radix select of the 512th largest key, most significant digit first.
+  // Radix select of the 512th largest key, most significant 11-bit digit
+  // first (thread i owns digits 2047 - 4i .. 2044 - 4i of the histogram).
   uint64_t prefix = 0, mask = 0;
   int need = kSparseBudget;
+  const int passes = (bits + kDigitBits - 1) / kDigitBits;
   for (int pass = 0; pass < passes; ++pass) {
-    const int shift = 8 * (passes - 1 - pass);
-    if (tid < 256) hist[tid] = 0;
+    const int shift = kDigitBits * (passes - 1 - pass);
+    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
     __syncthreads();
     for (int r = tid; r < R; r += kSelThreads) {
       const uint64_t key = rel_key(r);
-      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255)], 1);
+      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & (kBins - 1))], 1);
     }
     __syncthreads();
-    // Thread i < 256 looks at digit 255 - i: counts of higher digits before it.
-    const int cnt = tid < 256 ? hist[255 - tid] : 0;
-    const int incl = sel_scan_incl(cnt, wsum);
-    if (tid < 256 && incl >= need && incl - cnt < need) {
-      pick[0] = 255 - tid;
-      pick[1] = need - (incl - cnt);
+    int cnt[4], own = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cnt[k] = hist[kBins - 1 - (4 * tid + k)];
+      own += cnt[k];
+    }
+    int before = sel_scan_incl(own, wsum) - own;   // keys with higher digits than this thread's
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (before < need && before + cnt[k] >= need) {
+        pick[0] = kBins - 1 - (4 * tid + k);
+        pick[1] = need - before;
+      }
+      before += cnt[k];
     }
     __syncthreads();
     prefix |= (uint64_t)pick[0] << shift;
-    mask |= (uint64_t)255 << shift;
+    mask |= (uint64_t)(kBins - 1) << shift;
     need = pick[1];
     __syncthreads();
   }
