@@ -128,6 +128,15 @@ __device__ __forceinline__ intx4 apply_keep(intx4 v, const uint32_t* keep) {
 template <int N>
 using Int = std::integral_constant<int, N>;
 
+// f(Int<I>{}) for I = I0 .. N-1, unrolled at compile time.
+template <int I0, int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (I0 < N) {
+    f(Int<I0>{});
+    unroll<I0 + 1, N>(f);
+  }
+}
+
 // kK8 / kV8 (FP8 only): K / V^T tiles stay E4M3 codes in LDS and the
 // compute waves widen their operands; otherwise the loaders widen the codes
 // to bf16 as they publish a phase.  8-bit K tiles use the key <-> row map
@@ -173,8 +182,9 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   constexpr int kKSlot = kK8 ? kPhaseBytes / 2 : kPhaseBytes;   // LDS bytes of a K tile
   constexpr int kVSlot = kV8 ? kPhaseBytes / 2 : kPhaseBytes;   // and of a V^T tile
   // Phases in flight in the loaders' registers: 4 bf16 or 8 FP8 phases,
-  // 128 KB of cache data per CU either way.
-  constexpr int kStages = kFp8 ? 8 : 4;
+  // 128 KB of cache data per CU either way (6 FP8 phases for token pairs,
+  // whose twelve waves have 168 registers per lane).
+  constexpr int kStages = kFp8 ? (kTps == 2 ? 6 : 8) : 4;
   constexpr int kFirstTiles = kStages / 2;            // tiles the start-up loads touch
   __shared__ __attribute__((aligned(1024))) uint8_t kslot[kKSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t vslot[kVSlot];
@@ -638,16 +648,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
           if (q + I < nphase) step(ic, q + I, q + I + 1 + kStages < nphase);
         }
       };
-      one(Int<0>{});
-      one(Int<1>{});
-      one(Int<2>{});
-      one(Int<3>{});
-      if constexpr (kStages == 8) {
-        one(Int<4>{});
-        one(Int<5>{});
-        one(Int<6>{});
-        one(Int<7>{});
-      }
+      unroll<0, kStages>(one);
     };
     // Main loop: every load it issues is in range, so the issue pattern (and
     // the compiler's wait counts) is the same in every iteration.
