@@ -170,3 +170,31 @@ def test_whole_step_end_to_end():
         for g in range(4):
             assert np.array_equal(gsel[b, g, :gn[b, g]], refsel[b][g]), (b, g)
     assert_parity(out, ref, "bf16", "sparse step end to end")
+
+
+def test_bad_selections_are_clamped_into_the_candidates():
+    # Ids below 0 or past the candidates and counts outside [0, 512] are the
+    # caller's error; the kernel clamps them (id -> [0, R - 1], count ->
+    # [0, min(R, 512)]) and so reads only the request's own blocks.
+    case, idx = _case([4105, 300, 9])
+    R = [(int(L) - 1) // 8 for L in case.ctx_lens]
+    rng = np.random.default_rng(5)
+    sel = rng.integers(-50, 1000, size=(3, 4, 512)).astype(np.int32)
+    nsel = np.array([[600, 512, -3, 100], [40, 37, 1000, 0], [5, 0, 1, -1]], np.int32)
+    vs = v_by_subblock(case.v_cache)
+    q = _raw_to_tensor(case.q, "bf16", "cuda")
+    out = torch.full((3, 64, 192), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mfa.mfa_sparse_attention(q, _raw_to_tensor(case.k_cache, "bf16", "cuda"),
+                             _raw_to_tensor(vs, "bf16", "cuda"),
+                             torch.from_numpy(case.block_table).cuda(),
+                             torch.from_numpy(case.ctx_lens.astype(np.int32)).cuda(),
+                             torch.from_numpy(sel).cuda(), torch.from_numpy(nsel).cuda(), out,
+                             case.scale)
+    torch.cuda.synchronize()
+    ref = []
+    for b, L in enumerate(case.ctx_lens):
+        n = np.clip(nsel[b], 0, min(R[b], 512))
+        clamped = [np.clip(sel[b, g, :n[g]], 0, max(R[b] - 1, 0)) for g in range(4)]
+        ref.append(sparse_attention(case.q[b], case.k_cache, vs, case.block_table, b, int(L) - 1,
+                                    clamped, case.scale))
+    assert_parity(out, np.stack(ref), "bf16", "clamped selections")
