@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   // 128 KB of cache data per CU either way (6 FP8 phases for token pairs,
   // whose twelve waves have 168 registers per lane).
   constexpr int kStages = kFp8 ? (kTps == 2 ? 6 : 8) : 4;
-  constexpr int kFirstTiles = kStages / 2;            // tiles the start-up loads touch
+  constexpr int kFirstTiles = (kStages + 1) / 2;      // tiles the start-up loads touch
   __shared__ __attribute__((aligned(1024))) uint8_t kslot[kKSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t vslot[kVSlot];
   __shared__ int blk_ids[kMaxChunkTiles];
@@ -626,9 +626,10 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       store_phase(0, stage[0]);
       lds_barrier();   // block ids and phase 0 visible
     }
-    // Phase kStages into the freed stage (clamped to the last tile, same K/V
-    // parity, when the split is shorter; such a copy is never published).
-    load_phase_cached(min(kStages, nphase - 2), stage[0]);
+    // Phase kStages into the freed stage (clamped to the last phase of the
+    // same K/V parity when the split is shorter; such a copy is never
+    // published).
+    load_phase_cached(min(kStages, nphase - 2 + (kStages & 1)), stage[0]);
     // Step q: barrier q, publish phase q+1 (loaded kStages steps ago) into
     // its slot, load phase q+1+kStages into the registers it freed.  Phase
     // i lives in stage i % kStages; steps are unrolled kStages at a time.
