@@ -28,7 +28,7 @@ mfa_status validate(const mfa_sparse_desc* d) {
   if (!d) return MFA_ERR_NULL;
   if (d->out_dtype != MFA_BF16 && d->out_dtype != MFA_F32) return MFA_ERR_DTYPE;
   if (d->batch < 0 || d->batch > 16383 || d->max_blocks_per_seq <= 0 ||
-      d->max_blocks_per_seq * 8 > mfa::kSparseMaxCand || d->num_blocks < 0 || d->num_splits < 0 ||
+      d->max_blocks_per_seq > mfa::kSparseMaxCand / 8 || d->num_blocks < 0 || d->num_splits < 0 ||
       d->num_splits > mfa::kSparseMaxTiles)
     return MFA_ERR_SHAPE;
   return MFA_OK;

@@ -188,6 +188,10 @@ def test_sparse_entry_rules():
     assert att(None) == MFA_ERR_NULL
     assert att(sparse(out_dtype=MFA_FP8_E4M3)) == MFA_ERR_DTYPE
     assert att(sparse(max_blocks_per_seq=513)) == MFA_ERR_SHAPE         # > 4096 candidate blocks
+    # a table width whose candidate count overflows 32 bits is refused, not wrapped
+    for wide in (1 << 29, (1 << 31) - 1):
+        assert att(sparse(max_blocks_per_seq=wide)) == MFA_ERR_SHAPE
+        assert lib.mfa_sparse_workspace_size(ctypes.byref(sparse(max_blocks_per_seq=wide))) == 0
     assert att(sparse(num_splits=66)) == MFA_ERR_SHAPE
     assert att(sparse(num_blocks=0, num_splits=1)) == MFA_ERR_SHAPE
     assert att(sparse(), q=None) == MFA_ERR_NULL
