@@ -93,6 +93,12 @@ DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus
     const int64_t want = ceil_div(cus, units);
     const int64_t chunk = std::max<int64_t>(4, ceil_div(cap, want));
     splits = ceil_div(cap, chunk);
+    // A split adds the merge kernel and the boundary before it (~4-5 us on
+    // MI355X); it pays only when it takes enough work off each workgroup.
+    // Work is counted as bf16 K/V bytes per page (FP8 tiles cost about as
+    // much compute-wave time as bf16 ones), doubled for two-token slots.
+    const int64_t saved = (cap - ceil_div(cap, splits)) * 2 * kPage * d->head_dim * 2 * rows_per_head;
+    if (splits > 1 && saved < kMinSplitSavedBytes) splits = 1;
   }
   int64_t chunk = ceil_div(cap, splits);
   if (chunk > kMaxChunkPages) chunk = kMaxChunkPages;

@@ -34,6 +34,10 @@ struct DecodePlan {
 
 // Largest chunk a split may cover (block ids cached per workgroup).
 constexpr int32_t kMaxChunkPages = 2048;
+// Heuristic split counts: splitting must take at least this many bf16 K/V
+// bytes off each workgroup's share, else the call runs unsplit (measured on
+// MI355X: 384 KB saved per workgroup lost to the merge, 512 KB won).
+constexpr int64_t kMinSplitSavedBytes = 448 * 1024;
 // Workspace regions are aligned to this many bytes.
 constexpr size_t kWorkspaceAlign = 256;
 // Balanced partition limits: one scan lane per slot (a 512-thread

@@ -130,7 +130,11 @@ def test_workspace_size_matches_partials():
     (256, 64, 256, 0, 1),      # B=256 x 4K: no split needed
     (1, 64, 256, 0, 16),       # one slot: 16 chunks of 4 pages
     (2, 2, 256, 0, 1),         # tiny context: chunks never below 4 pages
-    (32, 512, 256, 512, 2),    # 512-key window touches <= 9 pages; 128 units -> 2 chunks
+    # A split must save >= 448 KB of bf16 K/V per workgroup:
+    (32, 512, 256, 512, 1),    # 512-key window, <= 9 pages: 2 chunks would save 192 KB
+    (64, 8, 256, 0, 1),        # B=64 x 512: 2 chunks would save 4 pages = 256 KB
+    (64, 12, 256, 0, 3),       # B=64 x 768: 3 chunks of 4 save 8 pages = 512 KB
+    (32, 16, 256, 1024, 1),    # GQA 1024-key window: 2 chunks would save 8 x 48 KB
 ])
 def test_split_heuristic(batch, blocks, cus, window, expect):
     lib = _lib.load()
