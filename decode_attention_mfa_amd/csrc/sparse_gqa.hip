@@ -242,10 +242,11 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
   for (int r = tid; r < R; r += kSelThreads) sc[r] = scg[r];
   __syncthreads();
 
-  // Keys relative to the smallest score: key = (mono(s) - mono(min)) << 12 |
-  // (4095 - id) keeps the order and drops the leading bits all scores share
-  // (sign, exponent), so the first radix digit already spreads the keys
-  // and only as many radix passes run as the spread needs.
+  // Keys relative to the smallest score: key = mono(s) - mono(min) keeps the
+  // order and drops the leading bits all scores share (sign, exponent), so
+  // the first radix digit already spreads the keys and only as many radix
+  // passes run as the spread needs (none when every score is equal).  Equal
+  // keys are told apart by block id at the end, lower ids first.
   uint32_t lo_m = 0xFFFFFFFFu, hi_m = 0;
   for (int r = tid; r < R; r += kSelThreads) {
     const uint32_t m = mono_bits(sc[r]);
@@ -270,13 +271,12 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
     hi_m = max(hi_m, (uint32_t)hist[w2]);
   }
   __syncthreads();
-  const int bits = 12 + (hi_m > lo_m ? 32 - __builtin_clz(hi_m - lo_m) : 0);
-  auto rel_key = [&](int r) {
-    return ((uint64_t)(mono_bits(sc[r]) - lo_m) << 12) | (uint64_t)(kSparseMaxCand - 1 - r);
-  };
-  // Radix select of the 512th largest key, most significant 11-bit digit
-  // first (thread i owns digits 2047 - 4i .. 2044 - 4i of the histogram).
-  uint64_t prefix = 0, mask = 0;
+  const int bits = hi_m > lo_m ? 32 - __builtin_clz(hi_m - lo_m) : 0;
+  auto rel_key = [&](int r) { return mono_bits(sc[r]) - lo_m; };
+  // Radix select of the 512th largest key T, most significant 11-bit digit
+  // first (thread i owns digits 2047 - 4i .. 2044 - 4i of the histogram);
+  // afterwards `need` counts the keys equal to T that are taken.
+  uint32_t prefix = 0, mask = 0;
   int need = kSparseBudget;
   const int passes = (bits + kDigitBits - 1) / kDigitBits;
   for (int pass = 0; pass < passes; ++pass) {
@@ -284,7 +284,7 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
     for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
     __syncthreads();
     for (int r = tid; r < R; r += kSelThreads) {
-      const uint64_t key = rel_key(r);
+      const uint32_t key = rel_key(r);
       if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & (kBins - 1))], 1);
     }
     __syncthreads();
@@ -304,24 +304,39 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
       before += cnt[k];
     }
     __syncthreads();
-    prefix |= (uint64_t)pick[0] << shift;
-    mask |= (uint64_t)(kBins - 1) << shift;
+    prefix |= (uint32_t)pick[0] << shift;
+    mask |= (uint32_t)(kBins - 1) << shift;
     need = pick[1];
     __syncthreads();
   }
-  // Keys at or above the 512th: exactly 512; written in ascending id order.
+  // Every key above T and the `need` lowest-id keys equal to T: exactly
+  // 512, written in ascending id order.  One scan carries both counts
+  // (above in the low 16 bits, equal in the high; each at most 4096).
   constexpr int kPer = kSparseMaxCand / kSelThreads;
   int mine = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int r = tid * kPer + k;
-    mine += (r < R && rel_key(r) >= prefix) ? 1 : 0;
+    if (r < R) {
+      const uint32_t key = rel_key(r);
+      mine += key > prefix ? 1 : (key == prefix ? 1 << 16 : 0);
+    }
   }
-  int pos = sel_scan_incl(mine, wsum) - mine;
+  const int before = sel_scan_incl(mine, wsum) - mine;
+  int eq_before = before >> 16;
+  int pos = (before & 0xFFFF) + min(eq_before, need);
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int r = tid * kPer + k;
-    if (r < R && rel_key(r) >= prefix) out[pos++] = r;
+    if (r < R) {
+      const uint32_t key = rel_key(r);
+      if (key > prefix) {
+        out[pos++] = r;
+      } else if (key == prefix) {
+        if (eq_before < need) out[pos++] = r;
+        ++eq_before;
+      }
+    }
   }
   if (tid == 0) p.nsel_out[bg] = kSparseBudget;
 }
