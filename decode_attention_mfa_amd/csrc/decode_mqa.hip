@@ -586,11 +586,13 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       }
       return;
     }
+    // Split partials are read once, by the merge kernel: streamed out rather
+    // than kept dirty in L2 for the write-back at the kernel's end.
     const int64_t row = piece * kRows + (head - g * kRows);
 #pragma unroll
     for (int ct = 0; ct < kD / 16; ++ct)
-      *reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4) = acc[ct];
-    if (q4 == 0) *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{m_run, l_tot};
+      __builtin_nontemporal_store(acc[ct], reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4));
+    if (q4 == 0) __builtin_nontemporal_store(floatx2{m_run, l_tot}, reinterpret_cast<floatx2*>(p.part_ml + row * 2));
   };
 
   if (!empty) {
