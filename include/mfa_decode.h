@@ -211,9 +211,11 @@ mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
 size_t mfa_decode_workspace_size(const mfa_decode_desc* desc, int32_t window);
 
 /* The split heuristic (host integers only): how many chunks each slot's key
- * range is cut into, given the device's compute-unit count.  Keeps
+ * range is cut into, given the device's compute-unit count.  Aims for
  * B * Hkv * splits at or above one wave of workgroups on `num_cus` compute
- * units while keeping chunks at least 256 keys long.  Returns >= 1, or 0 if
+ * units, with chunks at least 256 keys long, and runs unsplit (1) when the
+ * split would take less than 448 KB of bf16-sized K/V off each workgroup
+ * (the merge kernel would cost more than it saves).  Returns >= 1, or 0 if
  * desc is NULL or invalid. */
 int32_t mfa_decode_plan_splits(const mfa_decode_desc* desc, int32_t window, int32_t num_cus);
 
