@@ -131,3 +131,105 @@ def test_subset_matches_brute_force_softmax():
         p = np.exp(s - s.max())
         want = (p / p.sum()) @ np.array(v)
         assert np.allclose(got[h], want, rtol=0, atol=1e-12), h
+
+
+# --- the whole decode step (sparse_decode): token position, candidates, composition ---
+
+def _step_batch(lens, seed, nan_tail=True):
+    """A Step-5-shaped batch for sparse_decode: paged K, V^T per 8-token
+    sub-block, indexer inputs and the summary codes of the complete blocks."""
+    from oracle.sparse import sparse_decode  # noqa: F401  (imported by the callers)
+    from workloads import make_sparse_indexer_inputs
+    case = make_decode_case(seed, batch=len(lens), ctx_lens=lens, hq=64, hkv=4, d=192,
+                            kv_format="bf16", nan_tail=nan_tail)
+    cap = case.block_table.shape[1] * 64
+    idx = make_sparse_indexer_inputs(seed + 1, batch=len(lens), cap=cap)
+    codes = np.zeros((len(lens), cap // 8, 256), np.uint8)
+    for b, L in enumerate(lens):
+        _, c = block_summaries(bf16_bits_to_f64(idx.k_idx[b]), bf16_bits_to_f64(idx.z[b]), L)
+        codes[b, :len(c)] = c
+    return case, idx, codes
+
+
+def _bf16_bits(x):
+    return np.asarray(torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
+                      .view(torch.int16).numpy()).view(np.uint16)
+
+
+def test_step_with_every_candidate_selected_is_dense_attention():
+    # t = L - 1 has t // 8 candidate blocks; at most 512 of them (L <= 4104)
+    # are all selected, so with the current block the step attends every one
+    # of the L keys: dense attention over the whole context.
+    from oracle.sparse import sparse_decode
+    lens = [1, 7, 8, 9, 65, 1000, 4104, 0]
+    case, idx, codes = _step_batch(lens, seed=21)
+    out, sels = sparse_decode(case.q, idx.q_idx, idx.w, codes, case.k_cache,
+                              v_by_subblock(case.v_cache), case.block_table, case.ctx_lens,
+                              case.scale)
+    ref = decode_attention(case.q, case.k_cache, case.v_cache, case.ctx_lens, case.scale,
+                           q_format="bf16", kv_format="bf16", block_table=case.block_table)
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+    for b, L in enumerate(lens):
+        want = np.arange(max(L - 1, 0) // 8)
+        assert all(np.array_equal(s, want) for s in sels[b]), b
+    assert np.all(out[-1] == 0)                              # L == 0: zeros
+
+
+@pytest.mark.parametrize("L", [1, 8, 9, 16, 17, 4105, 8 * 600, 8 * 600 + 1])
+def test_step_attends_the_token_at_L_minus_1(L):
+    # Key L-1 (the decode token's own position) dominates every logit of its
+    # group by far more than fp64's exponent range: the step must return its
+    # value row exactly.  A step placing the token at L would read the
+    # NaN-filled row L; one placing it at L-2 would never attend row L-1.
+    from oracle.sparse import sparse_decode
+    case, idx, codes = _step_batch([L], seed=22)
+    q = np.zeros((1, 64, 192), np.float32)
+    q[0, :, 0] = 1.0
+    case.q = _bf16_bits(q)
+    blk, row = case.block_table[0, (L - 1) // 64], (L - 1) % 64
+    case.k_cache[blk, :, row, 0] = _bf16_bits(np.array([3.0e4], np.float32))[0]
+    out, _ = sparse_decode(case.q, idx.q_idx, idx.w, codes, case.k_cache,
+                           v_by_subblock(case.v_cache), case.block_table, case.ctx_lens,
+                           case.scale)
+    for g in range(4):
+        want = bf16_bits_to_f64(case.v_cache[blk, g, :, row])
+        assert np.array_equal(out[0, 16 * g:16 * (g + 1)], np.broadcast_to(want, (16, 192))), g
+
+
+def test_step_selects_from_the_right_queries_and_candidates():
+    # Summaries that are one-hot at coordinate 4b + g for a chosen set of 512
+    # blocks of request b and group g, and search queries of request b that
+    # are one-hot at those coordinates: each group's selection is its chosen
+    # set.  Block (L-1)//8 = t//8 holds the token, so it is no candidate even
+    # though its summary scores highest (L = 8k: a token placed at L would
+    # make it one).  Reading request 0's queries for request 1 selects
+    # request 0's sets instead.
+    from oracle.sparse import sparse_attention, sparse_decode
+    lens = [8 * 700, 8 * 650]
+    case, idx, codes = _step_batch(lens, seed=23, nan_tail=False)
+    rng = np.random.default_rng(24)
+    codes[:] = 0
+    q_idx = np.zeros((2, 4, 4, 256), np.float32)
+    w = np.ones((2, 4, 4), np.float32)
+    one = 0x38                                               # E4M3 code of 1.0
+    chosen = {}
+    for b, L in enumerate(lens):
+        cand = (L - 1) // 8
+        for g in range(4):
+            c = 4 * b + g
+            q_idx[b, g, :, c] = 1.0
+            chosen[b, g] = np.sort(rng.choice(cand, size=512, replace=False))
+            codes[b, chosen[b, g], c] = one
+            codes[b, cand, c] = 0x7E                          # 448 on the token's own block
+    idx.q_idx = _bf16_bits(q_idx)
+    out, sels = sparse_decode(case.q, idx.q_idx, w, codes, case.k_cache,
+                              v_by_subblock(case.v_cache), case.block_table, case.ctx_lens,
+                              case.scale)
+    for b, L in enumerate(lens):
+        for g in range(4):
+            assert np.array_equal(sels[b][g], chosen[b, g]), (b, g)
+        ref = sparse_attention(case.q[b], case.k_cache, v_by_subblock(case.v_cache),
+                               case.block_table, b, L - 1, [chosen[b, g] for g in range(4)],
+                               case.scale)
+        assert np.array_equal(out[b], ref)
