@@ -34,7 +34,13 @@ def _dtype_code(t, allow_fp8=False):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Data pointer of a tensor the library reads or writes as a dense
+    row-major array; a strided view would be read with the wrong strides."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError(f"tensor of shape {tuple(t.shape)} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(t, stream):
@@ -66,6 +72,9 @@ def decode_desc(q, k_cache, block_table, out, num_splits=0):
         num_blocks = k_cache.shape[0]
     else:
         hkv = k_cache.shape[2]
+        if k_cache.shape[1] % PAGE:
+            raise ValueError(f"a contiguous cache's capacity ({k_cache.shape[1]}) must be a "
+                             f"multiple of {PAGE} tokens")
         max_blocks = k_cache.shape[1] // PAGE
         num_blocks = 0
     return MfaDecodeDesc(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=PAGE,
@@ -184,6 +193,9 @@ def kv_append_desc(k_new, k_cache, block_table):
     if block_table is not None:
         max_blocks, num_blocks = block_table.shape[1], k_cache.shape[0]
     else:
+        if k_cache.shape[1] % PAGE:
+            raise ValueError(f"a contiguous cache's capacity ({k_cache.shape[1]}) must be a "
+                             f"multiple of {PAGE} tokens")
         max_blocks, num_blocks = k_cache.shape[1] // PAGE, 0
     return MfaKvAppendDesc(batch=B, num_kv_heads=hkv, head_dim=d, page_size=PAGE,
                            max_blocks_per_seq=max_blocks, num_blocks=num_blocks,

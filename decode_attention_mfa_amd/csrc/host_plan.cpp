@@ -45,6 +45,9 @@ mfa_status validate_decode_desc(const mfa_decode_desc* d, int32_t window, bool m
   if (d->num_q_heads % d->num_kv_heads != 0) return MFA_ERR_SHAPE;
   if (d->page_size != kPage) return MFA_ERR_SHAPE;
   if (d->max_blocks_per_seq <= 0 || d->num_splits < 0 || d->num_blocks < 0) return MFA_ERR_SHAPE;
+  // Upper bounds that keep the workspace arithmetic (rows x d x 4 bytes, in
+  // 64-bit) far from overflow for any accepted shape.
+  if (d->num_q_heads > kMaxQueryHeads || d->num_splits > kMaxForcedSplits) return MFA_ERR_SHAPE;
   if (mqa_entry && d->num_kv_heads != 1) return MFA_ERR_SHAPE;
   // One grid row per (slot, KV head) and one workgroup per (slot, head) on
   // the fp32 path: stay inside the 65535 limit of a grid's y dimension.
@@ -101,7 +104,9 @@ DecodePlan plan_decode(const mfa_decode_desc* d, int32_t window, int32_t num_cus
     if (splits > 1 && saved < kMinSplitSavedBytes) splits = 1;
   }
   int64_t chunk = ceil_div(cap, splits);
-  if (chunk > kMaxChunkPages) chunk = kMaxChunkPages;
+  // A split caches its block ids (the fp32 kernel walks the table itself and
+  // never splits).
+  if (pl.path != DecodePath::kF32 && chunk > kMaxChunkPages) chunk = kMaxChunkPages;
   splits = ceil_div(cap, chunk);
   pl.splits = (int32_t)splits;
   pl.chunk_pages = (int32_t)chunk;

@@ -34,6 +34,9 @@ struct DecodePlan {
 
 // Largest chunk a split may cover (block ids cached per workgroup).
 constexpr int32_t kMaxChunkPages = 2048;
+// Largest query-head count and forced split count a descriptor may carry.
+constexpr int32_t kMaxQueryHeads = 1024;
+constexpr int32_t kMaxForcedSplits = 16384;
 // Heuristic split counts: splitting must take at least this many bf16 K/V
 // bytes off each workgroup's share, else the call runs unsplit (measured on
 // MI355X: 384 KB saved per workgroup lost to the merge, 512 KB won).

@@ -112,6 +112,10 @@ mfa_status query_slot_desc(const mfa_decode_desc* d, int32_t tq, int32_t window,
   *tps = (tq % 2 == 0) ? 2 : 1;
   *vd = *d;
   vd->batch = d->batch * (tq / *tps);
+  // The query slots, not the sequences, set the grid: apply the size rules
+  // (the 65535 limit of a grid's y dimension among them) to them again.
+  st = mfa::validate_decode_desc(vd, window, mqa_entry);
+  if (st != MFA_OK) return st;
   if (tq > 1 && mfa::plan_decode(vd, window, 1).path != mfa::DecodePath::kMqaShared)
     return MFA_ERR_SHAPE;
   return MFA_OK;

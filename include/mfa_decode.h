@@ -29,8 +29,11 @@
  *               K: [B, cap, Hkv, d]             V: [B, Hkv, d, cap]
  *               with cap = max_blocks_per_seq * P
  *   Rows at positions >= L inside a slot's last block may hold anything,
- *   NaN included: they are never used.  Block-table entries past the last
- *   block a slot uses are never read (callers pad with -1).
+ *   NaN included: they never reach the result.  Block-table entries past the
+ *   last block a slot uses do not affect the result either, but the kernels
+ *   may read them ahead of the length (prefetch and speculation): they must
+ *   be readable memory, and whatever they hold is clamped into the pool
+ *   before any cache access (callers pad with -1, which reads block 0).
  *
  * Ownership, streams, graphs
  *   The caller owns every buffer (device memory for all data pointers).  The
@@ -85,7 +88,7 @@ typedef enum mfa_dtype {
 /*
  * Shape and type of one decode-attention call.
  *   batch               B >= 0 slots (B == 0 enqueues nothing)
- *   num_q_heads         Hq
+ *   num_q_heads         Hq, at most 1024
  *   num_kv_heads        Hkv, Hq % Hkv == 0
  *   head_dim            d
  *   page_size           tokens per cache block; must be 64
@@ -98,7 +101,10 @@ typedef enum mfa_dtype {
  *                       BF16 or F32; kv F32 with q F32 and out F32
  *   num_splits          0 = choose with the library's heuristic
  *                       (mfa_decode_plan_splits); > 0 forces that many splits
- *                       of each slot's key range.  With 0, a paged dense MQA
+ *                       of each slot's key range (at most the slot's pages,
+ *                       and at least enough that no split covers more than
+ *                       2048 pages, the block ids one split caches); at
+ *                       most 16384.  With 0, a paged dense MQA
  *                       call (Hkv == 1, B <= 512, at most 512 pages per
  *                       split) instead spreads the batch's actual pages
  *                       evenly over the same number of workgroups, reading

@@ -170,6 +170,12 @@ def test_multi_token_entry_rules():
     assert call_mtp(desc(), 2) == MFA_ERR_WORKSPACE               # forced splits need room
     assert call_mtp(desc(), 2, q=None) == MFA_ERR_NULL
     assert call_mtp(desc(batch=0), 3, q=None) == 0
+    # The query slots (batch x Tq/2 token pairs, or batch x Tq single tokens)
+    # set the launch grid: a batch inside the 65535 grid-row limit whose
+    # slots are not is a shape error, not a launch failure.
+    assert call_mtp(desc(batch=40000), 4) == MFA_ERR_SHAPE       # 80000 pair slots
+    assert call_mtp(desc(batch=30000), 3) == MFA_ERR_SHAPE       # 90000 single-token slots
+    assert call_mtp(desc(batch=32000), 2) == MFA_ERR_WORKSPACE   # 32000 slots: valid shape
     # The workspace of Tq tokens is that of Tq times as many single-token slots.
     for tq in (1, 2, 4):
         got = lib.mfa_decode_mtp_workspace_size(ctypes.byref(desc(num_splits=4)), tq)
@@ -224,3 +230,27 @@ def test_phase_entry_rules():
         assert lib.mfa_decode_attention_phase(ctypes.byref(desc()), A, A, A, A, A, None, None, A,
                                               ctypes.c_float(0.0625), None, ctypes.c_size_t(0),
                                               ctypes.c_int32(phase), None) == MFA_ERR_WORKSPACE
+
+
+def test_binding_rejects_strided_tensors_and_ragged_capacity():
+    # The binding hands the library bare data pointers: a strided view or a
+    # contiguous cache whose capacity is not whole 64-token blocks would be
+    # read with the wrong layout, so it refuses them before any call.
+    import torch
+    import decode_attention_mfa_amd as mfa
+    q = torch.zeros((2, 64, 256), dtype=torch.bfloat16)
+    k = torch.zeros((4, 1, 64, 256), dtype=torch.bfloat16)
+    v = torch.zeros((4, 1, 256, 64), dtype=torch.bfloat16)
+    table = torch.zeros((2, 2), dtype=torch.int32)
+    lens = torch.zeros((2,), dtype=torch.int32)
+    out = torch.zeros_like(q)
+    with pytest.raises(ValueError, match="contiguous"):
+        mfa.mfa_decode_attention(q.transpose(1, 2).contiguous().transpose(1, 2), k, v, table,
+                                 lens, out, 0.0625, num_splits=1)
+    with pytest.raises(ValueError, match="contiguous"):
+        mfa.mfa_decode_attention(q, k, v, table.t().contiguous().t(), lens, out, 0.0625,
+                                 num_splits=1)
+    kc = torch.zeros((2, 100, 1, 256), dtype=torch.bfloat16)      # capacity 100 tokens
+    vc = torch.zeros((2, 1, 256, 100), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="multiple of 64"):
+        mfa.mfa_decode_attention(q, kc, vc, None, lens, out, 0.0625, num_splits=1)
