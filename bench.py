@@ -56,12 +56,13 @@ def make_case(config):
     raise SystemExit(f"unknown --config {config}")
 
 
-def cpu_baseline(case, budget_s):
+def cpu_baseline(case, budget_s, single_thread_s=0.0):
     """The oracle as it stands, on the host cores: it evaluates the slots of
     the same workload one after another (cycling through the batch) until
     about budget_s seconds have passed; one slot evaluation is one query
-    token's decode-attention step."""
-    from threadpoolctl import threadpool_info
+    token's decode-attention step.  A second, shorter run limits the BLAS
+    pool to one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import decode_attention
     q = case.q
     if q is None:   # FP8 config: q comes from the query path; time attention on a drawn q
@@ -69,18 +70,32 @@ def cpu_baseline(case, budget_s):
         rng = np.random.default_rng(404)
         q = bf16_round_bits(rng.standard_normal((case.batch, case.hq, case.d), dtype=np.float32))
     kw = case.oracle_kwargs()
-    done = 0
-    t0 = time.perf_counter()
-    while (time.perf_counter() - t0) < budget_s:
-        decode_attention(q, case.k_cache, case.v_cache, case.ctx_lens, case.scale,
-                         slots=[done % case.batch], **kw)
-        done += 1
-    el = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": done / el, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} slot evaluations ({done / case.batch:.1f} passes over the "
-                      f"{case.batch} slots of the same workload), fp64 numpy oracle, {el:.1f} s",
-            "host_cpu_count": os.cpu_count()}
+
+    def run(seconds):
+        done = 0
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) < seconds:
+            decode_attention(q, case.k_cache, case.v_cache, case.ctx_lens, case.scale,
+                             slots=[done % case.batch], **kw)
+            done += 1
+        return done, time.perf_counter() - t0
+
+    done, el = run(budget_s)
+    info = threadpool_info()
+    blas = [i for i in info if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    res = {"value": done / el, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} slot evaluations ({done / case.batch:.1f} passes over the "
+                     f"{case.batch} slots of the same workload), fp64 numpy oracle, {el:.1f} s",
+           "host_cpu_count": os.cpu_count(),
+           "blas": [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '')}"
+                    f"{', ' + i['architecture'] if i.get('architecture') else ''})" for i in blas]}
+    if single_thread_s > 0:
+        with threadpool_limits(limits=1, user_api="blas"):
+            done1, el1 = run(single_thread_s)
+        res["single_thread"] = {"value": done1 / el1, "unit": "query tokens/s", "cores": 1,
+                                "sample": f"{done1} slot evaluations, {el1:.1f} s"}
+    return res
 
 
 # Sources whose change invalidates the committed counter summary.
@@ -277,7 +292,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--pools", type=int, default=4)
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph instead of launching it")
@@ -316,8 +331,7 @@ def main():
     import torch
     import decode_attention_mfa_amd as mfa
     from decode_attention_mfa_amd import accounting
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import to_device
+    from workloads.torch_io import to_device
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -421,25 +435,43 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     call_ms = start.elapsed_time(end) / args.steps
 
-    # The attention kernel alone (the roofline's kernel): a second pass of
-    # the same K steps launched in their two phases, a HIP event pair on the
-    # launch stream around each attention launch (the merge runs after it).
+    # Per-call distribution (the survey's protocol): a HIP event pair around
+    # every step of a second pass.  The markers add their own packets between
+    # the kernels, so these figures sit a few microseconds above the
+    # back-to-back mean; they are reported for the spread, not as the rate.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        pairs[i][0].record(stream)
+        step(i)
+        pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+
+    # The attention kernel alone (the roofline's kernel): K back-to-back
+    # launches of the call's first phase (attention without the merge) under
+    # one event pair on the launch stream, rotating through the pool copies
+    # like the steps.  No marker sits between the launches, so the mean is
+    # the kernel's own duration plus the dispatch gap, as rocprofv3 sees it.
     kernel_ms = None
     if tq == 1 and case.hkv == 1 and window == 0 and not args.graph and not args.with_append:
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
+        kw = dict(k_scale=t["k_scale"], v_scale=t["v_scale"], num_splits=args.num_splits)
+
+        def attention_only(i):
             k, v = pools[i % len(pools)]
-            kw = dict(k_scale=t["k_scale"], v_scale=t["v_scale"], num_splits=args.num_splits)
-            pairs[i][0].record(stream)
             mfa.mfa_decode_attention_phase(t["q"], k, v, t["table"], t["lens"], out, case.scale, 1,
                                            **kw)
-            pairs[i][1].record(stream)
-            mfa.mfa_decode_attention_phase(t["q"], k, v, t["table"], t["lens"], out, case.scale, 2,
-                                           **kw)
+        for i in range(max(args.warmup, len(pools))):
+            attention_only(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+        e0.record(stream)
+        for i in range(args.steps):
+            attention_only(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kernel_ms = e0.elapsed_time(e1) / args.steps
 
     fmt_kv = case.kv_format
     append_bytes = 0
@@ -495,6 +527,11 @@ def main():
         "hbm_gbps": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "call_us_mean": call_ms * 1e3,
+        "call_us_percentiles": {
+            "p10": float(np.percentile(per_call_us, 10)), "p50": float(np.median(per_call_us)),
+            "p90": float(np.percentile(per_call_us, 90)),
+            "timed": "a HIP event pair around each step of a second pass (markers between "
+                     "the steps add their own time)"},
         "algorithmic_bytes_per_call": nbytes,
         "append_bytes_per_call": append_bytes,
         "flops_per_call": flops,
@@ -504,10 +541,10 @@ def main():
                      "kernel_us": kernel_ms * 1e3 if kernel_ms else None,
                      "step_achieved": achieved, "step_frac": achieved / HBM_PEAK_GBPS,
                      "traffic": committed_traffic(args.config) if tq == 1 else None,
-                     "timed": ("the attention kernel: a HIP event pair on the launch stream "
-                               "around each of its K launches, in a second pass of the K steps "
-                               "launched in two phases; step_*: one event pair around the timed "
-                               "steps (attention + merge)") if kernel_ms else (
+                     "timed": ("the attention kernel: one HIP event pair on the launch stream "
+                               "around K back-to-back launches of the call's attention phase "
+                               "(no merge, no marker between launches); step_*: one event pair "
+                               "around the K timed steps (attention + merge)") if kernel_ms else (
                               "one HIP event pair around the timed steps on the launch "
                               "stream, divided by the step count (attention kernel + split "
                               "merge kernel per step" + (", after the KV append)" if
@@ -515,7 +552,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample of the same workload")
-        res["cpu_baseline"] = cpu_baseline(cpu_case, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cpu_case, args.cpu_seconds,
+                                           single_thread_s=args.cpu_seconds / 2)
     print(json.dumps(res), flush=True)
 
 

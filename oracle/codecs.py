@@ -36,7 +36,11 @@ def e4m3fn_codes_to_f64(codes):
 
 
 def decode_storage(raw, fmt):
-    """Decode a raw storage array: fmt in {"f32", "bf16", "e4m3"}."""
+    """Decode a raw storage array: fmt in {"f32", "bf16", "e4m3"}, or "f64" for
+    values that are already exact (the query path's fp64 output handed to the
+    attention unrounded when the two steps are checked as one chain)."""
+    if fmt == "f64":
+        return np.asarray(raw, dtype=np.float64)
     if fmt == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if fmt == "bf16":

@@ -5,36 +5,10 @@ import numpy as np
 import torch
 
 import decode_attention_mfa_amd as mfa
+from workloads.torch_io import raw_to_tensor as _raw_to_tensor, to_device  # noqa: F401
 
 # Parity bars: bf16 / FP8 inputs -> max-abs 2e-2 and rel-L2 5e-3; fp32 -> 1e-4.
 TOL = {"bf16": (2e-2, 5e-3), "e4m3": (2e-2, 5e-3), "f32": (1e-4, 1e-4)}
-
-
-def _raw_to_tensor(arr, fmt, device):
-    if fmt == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
-    if fmt == "e4m3":
-        return torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn).to(device)
-    if fmt == "f32":
-        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
-    raise ValueError(fmt)
-
-
-def to_device(case, device="cuda", out_format=None):
-    out_format = out_format or case.out_format
-    t = {
-        "q": _raw_to_tensor(case.q, case.q_format, device) if case.q is not None else None,
-        "k": _raw_to_tensor(case.k_cache, case.kv_format, device),
-        "v": _raw_to_tensor(case.v_cache, case.kv_format, device),
-        "table": (torch.from_numpy(case.block_table).to(device)
-                  if case.block_table is not None else None),
-        "lens": torch.from_numpy(case.ctx_lens.astype(np.int32)).to(device),
-        "k_scale": (torch.from_numpy(case.k_scale).to(device) if case.k_scale is not None else None),
-        "v_scale": (torch.from_numpy(case.v_scale).to(device) if case.v_scale is not None else None),
-    }
-    odt = torch.float32 if out_format == "f32" else torch.bfloat16
-    t["out"] = torch.full((case.batch, case.hq, case.d), float("nan"), dtype=odt, device=device)
-    return t
 
 
 def run_decode(case, t, *, num_splits=0, window=None, q=None, lens=None, table=None):
@@ -61,11 +35,24 @@ def errors(got, ref):
     return max_abs, rel_l2
 
 
-def assert_parity(got, ref, fmt, what=""):
+def assert_parity(got, ref, fmt, what="", per_slot=False):
+    """Whole-tensor max-abs and relative-L2 within the bar of ``fmt``; with
+    per_slot, every slot (leading index) must also meet it on its own.  The
+    message names the worst slot."""
     max_abs_tol, rel_tol = TOL[fmt]
     g = got.detach().float().cpu().numpy()
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     max_abs, rel_l2 = errors(got, ref)
-    assert max_abs <= max_abs_tol and rel_l2 <= rel_tol, (
-        f"{what}: max_abs={max_abs:.3e} (tol {max_abs_tol}) rel_l2={rel_l2:.3e} (tol {rel_tol})")
+    gg = g.astype(np.float64).reshape(g.shape[0], -1)
+    rr = np.asarray(ref, dtype=np.float64).reshape(g.shape[0], -1)
+    slot_abs = np.abs(gg - rr).max(axis=1) if gg.size else np.zeros(0)
+    norms = np.linalg.norm(rr, axis=1)
+    slot_rel = np.linalg.norm(gg - rr, axis=1) / np.where(norms > 0, norms, 1.0)
+    worst = int(np.argmax(slot_rel)) if len(slot_rel) else -1
+    msg = (f"{what}: max_abs={max_abs:.3e} (tol {max_abs_tol}) rel_l2={rel_l2:.3e} (tol {rel_tol}); "
+           f"worst slot {worst}: max_abs={slot_abs[worst] if worst >= 0 else 0:.3e} "
+           f"rel_l2={slot_rel[worst] if worst >= 0 else 0:.3e}")
+    assert max_abs <= max_abs_tol and rel_l2 <= rel_tol, msg
+    if per_slot:
+        assert np.all(slot_abs <= max_abs_tol) and np.all(slot_rel <= rel_tol), msg
     return max_abs, rel_l2

@@ -3,7 +3,7 @@ scales, codes converted to bf16 on the way to LDS) against the fp64 oracle.
 
 Covers ragged lengths with NaN tail codes, every split count, fp32 output, the
 contiguous cache, the windowed path, the full-size 256 x 4096 batch on
-sampled slots, and a bit-exact check of the conversion of every finite code:
+every slot (alone and fed by the query path), block permutations bit for bit, and a bit-exact check of the conversion of every finite code:
 with a one-hot attention pattern the output is exactly the decoded V row."""
 
 import numpy as np
@@ -83,16 +83,71 @@ def test_every_finite_code_decodes_exactly(jstar, splits):
     np.testing.assert_array_equal(got, ref.astype(np.float32))
 
 
-def test_config4_full_size_sampled_slots():
-    """256 slots x 4096 keys, E4M3 K/V with per-head scales (drawn on the device)."""
+def _every_slot_oracle(dc, q_raw=None, q_format="bf16", chunk=64):
+    """The oracle over every slot of a device case, copied back a chunk of
+    slots at a time; q_raw replaces the case's query (format q_format)."""
+    refs = []
+    for s0 in range(0, dc.batch, chunk):
+        slots = list(range(s0, min(dc.batch, s0 + chunk)))
+        sub = dc.host_slots(slots)
+        kw = sub.oracle_kwargs()
+        kw["q_format"] = q_format
+        q = sub.q if q_raw is None else q_raw[slots]
+        refs.append(decode_attention(q, sub.k_cache, sub.v_cache, sub.ctx_lens, sub.scale, **kw))
+    return np.concatenate(refs)
+
+
+def test_config4_full_size_every_slot():
+    """256 slots x 4096 keys, E4M3 K/V with per-head scales (drawn on the
+    device), one split per slot as the benchmark runs it; every slot."""
     dc = make_device_case(4, batch=256, ctx_lens=[4096] * 256, hq=64, hkv=1, d=256,
                           kv_format="e4m3", scale=1 / 16, name="c4")
     out = torch.full((256, 64, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
     mfa.mfa_decode_attention(dc.q, dc.k, dc.v, dc.table, dc.lens, out, dc.scale,
                              k_scale=dc.k_scale, v_scale=dc.v_scale)
     torch.cuda.synchronize()
-    slots = [0, 100, 255]
-    sub = dc.host_slots(slots)
-    ref = decode_attention(sub.q, sub.k_cache, sub.v_cache, sub.ctx_lens, sub.scale,
-                           **sub.oracle_kwargs())
-    assert_parity(out[slots], ref, "e4m3", "config 4 sampled")
+    assert_parity(out, _every_slot_oracle(dc), "e4m3", "config 4", per_slot=True)
+
+
+def test_config4_query_path_into_fp8_attention_every_slot():
+    """Config 4 as one chain: the low-rank query path (x [256, 7168] ->
+    W_qdown -> RMSNorm -> W_qup -> 64 x 256, bf16 weights) feeds FP8-cache
+    attention on the device, against the oracle's query path feeding its
+    attention with the exact fp64 query ("Step-3 is Large yet Affordable",
+    section 2).  The library's query is bf16, so its rounding is inside the
+    tolerance here, unlike the per-step tests."""
+    from oracle import query_proj
+    from workloads import config_query_inputs
+    qi = config_query_inputs(4, batch=256)
+    dev = "cuda"
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.empty((256, 64 * 256), dtype=torch.bfloat16, device=dev)
+    mfa.mfa_query_proj(bf16(qi.x), bf16(qi.w_down.T), bf16(qi.w_up.T), q, num_heads=64,
+                       eps=qi.eps)
+    dc = make_device_case(4, batch=256, ctx_lens=[4096] * 256, hq=64, hkv=1, d=256,
+                          kv_format="e4m3", scale=1 / 16, name="c4")
+    out = torch.full((256, 64, 256), float("nan"), dtype=torch.bfloat16, device=dev)
+    mfa.mfa_decode_attention(q.view(256, 64, 256), dc.k, dc.v, dc.table, dc.lens, out, dc.scale,
+                             k_scale=dc.k_scale, v_scale=dc.v_scale)
+    torch.cuda.synchronize()
+    q_ref = query_proj(qi.x, qi.w_down, qi.w_up, fmt="bf16", eps=qi.eps, num_heads=64,
+                       head_dim=256)
+    ref = _every_slot_oracle(dc, q_raw=q_ref, q_format="f64")
+    assert_parity(out, ref, "e4m3", "config 4 chain", per_slot=True)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_fp8_block_permutation_is_bit_exact(splits):
+    # The same logical cache in the pool's identity order and shuffled: the
+    # block-table walk must give bit-identical outputs.
+    kw = dict(batch=4, ctx_lens=[777, 64, 2049, 4096], hq=64, hkv=1, d=256,
+              kv_format="e4m3", scale=1 / 16)
+    a = make_decode_case(94, shuffle=False, **kw)
+    b = make_decode_case(94, shuffle=True, **kw)
+    assert not np.array_equal(a.block_table, b.block_table)
+    assert np.array_equal(a.k_scale, b.k_scale) and np.array_equal(a.v_scale, b.v_scale)
+    ga = run_decode(a, to_device(a), num_splits=splits).clone()
+    gb = run_decode(b, to_device(b), num_splits=splits).clone()
+    assert torch.equal(ga.view(torch.int16), gb.view(torch.int16))

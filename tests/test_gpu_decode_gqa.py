@@ -7,7 +7,8 @@ layers attend to a 512-token window, the global layer to everything), a
 head, width 256) with a window, which runs the shared-tile kernel's windowed
 path.  Ragged lengths straddle the window and the 64-key blocks; tail rows
 past each length are NaN.  The full-size layer (32 slots x 32768 keys) is
-drawn on the device and checked on sampled slots.
+drawn on the device and checked on every slot; block permutations must leave
+the output bit for bit unchanged.
 """
 
 import numpy as np
@@ -83,17 +84,36 @@ def test_window_of_one_returns_the_last_value_row_exactly():
 
 
 @pytest.mark.parametrize("window", [512, 0])
-def test_step5_full_size_sampled_slots(window):
-    """32 slots x 32768 keys, 4 KV groups of width 192 (1.6 GB of bf16 K/V)."""
+def test_step5_full_size_every_slot(window):
+    """32 slots x 32768 keys, 4 KV groups of width 192 (1.6 GB of bf16 K/V),
+    local (512-key window) and global (dense) layer; every slot against the
+    oracle, copied back eight slots at a time."""
     dc = make_device_case(5, batch=32, ctx_lens=[32768] * 32, hq=64, hkv=4, d=192,
                           window=window, name="step5")
     out = torch.full((32, 64, 192), float("nan"), dtype=torch.bfloat16, device="cuda")
     mfa.mfa_decode_attention_gqa(dc.q, dc.k, dc.v, dc.table, dc.lens, out, dc.scale,
                                  window=window)
     torch.cuda.synchronize()
-    slots = [0, 13, 31]
-    sub = dc.host_slots(slots)
-    ref = decode_attention(sub.q, sub.k_cache, sub.v_cache, sub.ctx_lens, sub.scale,
-                           **sub.oracle_kwargs())
-    assert_parity(out[slots], ref, "bf16", f"step5 full window={window}")
+    refs = []
+    for s0 in range(0, 32, 8):
+        sub = dc.host_slots(list(range(s0, s0 + 8)))
+        refs.append(decode_attention(sub.q, sub.k_cache, sub.v_cache, sub.ctx_lens, sub.scale,
+                                     **sub.oracle_kwargs()))
+        del sub
+    assert_parity(out, np.concatenate(refs), "bf16", f"step5 full window={window}",
+                  per_slot=True)
     del dc
+
+
+@pytest.mark.parametrize("window", [0, 512])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_gqa_block_permutation_is_bit_exact(window, splits):
+    # Step-5 shape (4 groups of width 192): the same logical cache in the
+    # pool's identity order and shuffled gives bit-identical outputs.
+    kw = dict(batch=4, ctx_lens=[777, 64, 2049, 513], hq=64, hkv=4, d=192, window=window)
+    a = make_decode_case(95, shuffle=False, **kw)
+    b = make_decode_case(95, shuffle=True, **kw)
+    assert not np.array_equal(a.block_table, b.block_table)
+    ga = run_decode(a, to_device(a), num_splits=splits).clone()
+    gb = run_decode(b, to_device(b), num_splits=splits).clone()
+    assert torch.equal(ga.view(torch.int16), gb.view(torch.int16))

@@ -3,7 +3,7 @@
 All calls go through the C ABI (binding -> libmfa_decode.so).  Sizes are ones
 the oracle finishes in seconds while spanning several 64-key tiles, ragged
 tails (NaN-filled past each length), empty slots and every split count; the
-full-size configurations are checked on sampled slots.  Bit-exact checks:
+full-size configurations are checked on every slot.  Bit-exact checks:
 block permutation, single key, one-hot logits, repeat runs.
 """
 
@@ -64,23 +64,22 @@ def test_mqa_fp32_output():
     assert_parity(got, oracle(case), "bf16", "fp32 out")
 
 
-def test_config2_full_size_sampled_slots():
+def test_config2_full_size_every_slot():
+    # 64 slots x 4096 keys with the heuristic split count: the balanced page
+    # cut and the merge the benchmark runs, every slot against the oracle.
     case = config_case(2)
     t = to_device(case)
     got = run_decode(case, t)
-    slots = [0, 17, 42, 63]
-    assert_parity(got[slots], oracle(case, slots=slots), "bf16", "config 2 sampled")
-    assert torch.isfinite(got.float()).all()
+    assert_parity(got, oracle(case), "bf16", "config 2", per_slot=True)
 
 
-def test_config3_ragged_full_size_sampled_slots():
+def test_config3_ragged_full_size_every_slot():
+    # 128 ragged slots: pieces spanning several workgroups, workgroups
+    # walking several slots, non-first pieces; every slot against the oracle.
     case = config_case(3)
     t = to_device(case)
     got = run_decode(case, t)
-    order = np.argsort(case.ctx_lens)
-    slots = [int(order[0]), int(order[len(order) // 2]), int(order[-1]), 5]
-    assert_parity(got[slots], oracle(case, slots=slots), "bf16", "config 3 sampled")
-    assert torch.isfinite(got.float()).all()
+    assert_parity(got, oracle(case), "bf16", "config 3", per_slot=True)
 
 
 def test_block_permutation_is_bit_exact():

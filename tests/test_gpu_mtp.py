@@ -79,12 +79,10 @@ def test_contiguous_cache():
     assert_parity(out, _ref(case, q), "bf16", "mtp contiguous")
 
 
-def test_step3_shape_two_tokens_sampled():
+def test_step3_shape_two_tokens_every_slot():
     # B=64 sequences of 4096 keys, two new tokens each (MTP with one draft),
-    # heuristic splits as the bench runs it; sampled sequences vs the oracle.
+    # heuristic splits as the bench runs it; every sequence vs the oracle.
     case = make_decode_case(87, batch=64, ctx_lens=[4096] * 64, kv_format="bf16")
     q = make_mtp_queries(88, batch=64, tq=2)
     out, _ = _run(case, q, 2)
-    assert torch.isfinite(out.float()).all()
-    slots = [0, 21, 63]
-    assert_parity(out[slots], _ref(case, q, slots=slots), "bf16", "mtp B=64 L=4096 Tq=2")
+    assert_parity(out, _ref(case, q), "bf16", "mtp B=64 L=4096 Tq=2", per_slot=True)

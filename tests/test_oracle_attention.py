@@ -364,3 +364,21 @@ def test_empty_slot_gives_zeros_and_tails_are_never_read():
     out = _run(case)
     assert np.all(out[0] == 0)
     assert np.all(np.isfinite(out))
+
+
+def test_f64_query_is_taken_exactly():
+    # The "f64" query format hands exact values to the definition: for queries
+    # that are float32 values it equals the "f32" format bit for bit, and a
+    # query off the float32 grid changes the result (nothing is rounded).
+    case = make_decode_case(41, batch=2, ctx_lens=[70, 3], hq=8, hkv=2, d=64, kv_format="bf16")
+    rng = np.random.default_rng(42)
+    q32 = rng.standard_normal((2, 8, 64)).astype(np.float32)
+    kw = case.oracle_kwargs()
+    kw.pop("q_format")
+    a = decode_attention(q32, case.k_cache, case.v_cache, case.ctx_lens, 0.125, q_format="f32", **kw)
+    b = decode_attention(q32.astype(np.float64), case.k_cache, case.v_cache, case.ctx_lens, 0.125,
+                         q_format="f64", **kw)
+    assert np.array_equal(a, b)
+    q64 = q32.astype(np.float64) + 1e-12
+    c = decode_attention(q64, case.k_cache, case.v_cache, case.ctx_lens, 0.125, q_format="f64", **kw)
+    assert not np.array_equal(a, c)
