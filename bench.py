@@ -291,6 +291,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--pools", type=int, default=4)
+    ap.add_argument("--prewarm", type=float, default=0.3,
+                    help="seconds of untimed steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -398,6 +400,20 @@ def main():
                                          window=window, k_scale=t["k_scale"],
                                          v_scale=t["v_scale"], num_splits=args.num_splits)
 
+    # Untimed pre-warm: the GPU raises its clocks over a few hundred
+    # microseconds of load, so the same step is run for args.prewarm seconds
+    # before the warmup steps; the timed steps then see steady-state clocks
+    # (a handful of warmup steps alone left the first timed steps 10-20 %
+    # slower than the rest).
+    log(f"bench: pre-warm {args.prewarm:.2f} s")
+    t_end = time.perf_counter() + args.prewarm
+    i = 0
+    while time.perf_counter() < t_end:
+        call(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     log(f"bench: warmup {args.warmup}")
     for i in range(max(args.warmup, len(pools))):
         call(i)
@@ -523,6 +539,7 @@ def main():
                    "kv_heads": case.hkv, "head_dim": case.d, "kv_dtype": fmt_kv,
                    "page": 64, "window": window, "splits": splits, "kv_pool_copies": len(pools),
                    "launch": "hip graph replay" if args.graph else "eager",
+                   "prewarm_s": args.prewarm,
                    "append": bool(args.with_append), "query_tokens_per_slot": tq},
         "hbm_gbps": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,

@@ -125,6 +125,10 @@ __device__ __forceinline__ intx4 apply_keep(intx4 v, const uint32_t* keep) {
   return v;
 }
 
+// Every lambda of the kernels below is forced inline: one that the compiler
+// outlines (store_result, called at two sites) makes everything it captures
+// by reference live in scratch memory, the O^T accumulators included, which
+// then make a round trip through memory on every tile.
 template <int N>
 using Int = std::integral_constant<int, N>;
 
@@ -250,13 +254,13 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   const int64_t vgstep = (int64_t)(kFp8 ? 64 : 32) * p.v_row_stride * kElem;
   // LDS position of stored chunk c (16 codes or 8 bf16) of K row
   // krow0 + (8 or 16) k.
-  auto klds = [&](int k, int c) {
+  auto klds = [&](int k, int c) __attribute__((always_inline)) {
     const int row = krow0 + (kFp8 ? 16 : 8) * k;
     return kK8 ? (uint32_t)(row * 256 + ((c ^ swz_k8(row)) << 4))
                : (uint32_t)(row * 512 + ((c ^ swz_k(row)) << 4));
   };
   // V^T rows step by 32 or 64: the swizzle of the first row holds for all.
-  auto vlds = [&](int k, int c) {
+  auto vlds = [&](int k, int c) __attribute__((always_inline)) {
     const int row = vrow0 + (kFp8 ? 64 : 32) * k;
     return kV8 ? (uint32_t)(row * 64 + ((c ^ swz_v8(vrow0)) << 4))
                : (uint32_t)(row * 128 + ((c ^ swz_v(vrow0)) << 4));
@@ -264,7 +268,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
 
   // Register-staged loads of one phase (tiles clamped into the table row:
   // the start-up loads may run past the split).
-  auto load_phase = [&](int ph, intx4* st, int blk) {
+  auto load_phase = [&](int ph, intx4* st, int blk) __attribute__((always_inline)) {
     const int tile = min(t_begin + (ph >> 1), p.max_blocks - 1);
     if ((ph & 1) == 0) {
       const char* base =
@@ -283,7 +287,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
         st[k] = __builtin_nontemporal_load(reinterpret_cast<const intx4*>(base + k * vgstep));
     }
   };
-  auto load_phase_cached = [&](int ph, intx4* st) {
+  auto load_phase_cached = [&](int ph, intx4* st) __attribute__((always_inline)) {
     load_phase(ph, st, p.block_table ? readfirstlane(blk_ids[ph >> 1]) : 0);
   };
 
@@ -291,10 +295,10 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   // cache rows may hold anything, NaN included), so the PV product never
   // multiplies garbage by a zero probability.  A bf16 chunk holds 8
   // consecutive keys of one channel (vc*8 .. vc*8+7; FP8: 16 keys vc*16 ..).
-  auto store_phase = [&](int ph, const intx4* st) {
+  auto store_phase = [&](int ph, const intx4* st) __attribute__((always_inline)) {
     if (ph >= nphase) return;
     // Keys of this tile below the slot end (read for V^T phases only).
-    auto keys_of = [&]() { return kBal ? (int)tile_keys[ph >> 1] : L - (t_begin + (ph >> 1)) * kPage; };
+    auto keys_of = [&]() __attribute__((always_inline)) { return kBal ? (int)tile_keys[ph >> 1] : L - (t_begin + (ph >> 1)) * kPage; };
     if ((ph & 1) == 0) {
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
@@ -332,7 +336,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   intx4 stage[kStages][kPerThread];
   // The first kStages phases, block ids straight from the table, or (balanced
   // partition, other cut) from the tile list, clamped to its last tile.
-  auto load_first = [&](bool from_list) {
+  auto load_first = [&](bool from_list) __attribute__((always_inline)) {
 #pragma unroll
     for (int ph = 0; ph < kStages; ++ph)
       load_phase(ph, stage[ph],
@@ -353,7 +357,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   // wave parks its fragments in its own LDS rows and reads them back per K
   // tile, so that they are not held across the V phase.
   intx4 qf[kD / 32];
-  auto load_q = [&]() {
+  auto load_q = [&]() __attribute__((always_inline)) {
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD;
 #pragma unroll
     for (int c = 0; c < kD / 32; ++c) {
@@ -365,7 +369,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       for (int c = 0; c < kD / 32; ++c) qlds[(wave * (kD / 32) + c) * 64 + lane] = qf[c];
     }
   };
-  auto qfrag = [&](int c) {
+  auto qfrag = [&](int c) __attribute__((always_inline)) {
     if constexpr (kTps == 1)
       return qf[c];
     else
@@ -418,7 +422,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       for (int k = 0; k < kTpt; ++k)
         spec_ids[k] = spec_row[min(spec_pg + tid + k * kCt, p.max_blocks - 1)];
       // The compute waves only: wait until all have passed sync point n.
-      auto cw_sync = [&](int n) {
+      auto cw_sync = [&](int n) __attribute__((always_inline)) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         if (lane == 0) __hip_atomic_fetch_add(bal_sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         while (__hip_atomic_load(bal_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kCw * n)
@@ -481,7 +485,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       cw_sync(2);
       const int nt_here = min(e_w - s_w, kMaxBalancedTiles);
       // Slot of global page x: the last slot starting at or before it.
-      auto slot_of = [&](int x) {
+      auto slot_of = [&](int x) __attribute__((always_inline)) {
         int lo_s = 0, hi_s = p.batch - 1;
         while (lo_s < hi_s) {
           const int mid = (lo_s + hi_s + 1) >> 1;
@@ -532,7 +536,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   const int lo = (!kDense && L > p.window) ? L - p.window : 0;
   // Keys this compute wave's token attends: the slot's (its last token's)
   // length, one fewer for the first token of a pair.
-  auto query_keys = [&](int len) { return kTps == 1 ? len : max(len - (kTps - 1 - tk), 0); };
+  auto query_keys = [&](int len) __attribute__((always_inline)) { return kTps == 1 ? len : max(len - (kTps - 1 - tk), 0); };
   int Lq = query_keys(L);
   int n_tiles = 0, t_lo = 0;
   if (L > 0) {
@@ -569,7 +573,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
 
   // A compute wave holds every key of its 16 heads for the piece it has
   // walked: the final output of slot b, or partial `piece` for the merge.
-  auto store_result = [&](bool final_out, int64_t piece) {
+  auto store_result = [&](bool final_out, int64_t piece) __attribute__((always_inline)) {
     const float l_tot = wave_sum_xor16_32(l_run);
     if (final_out) {
       // (The first token of a pair may have no key at all: zeros.)
@@ -635,15 +639,15 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
     // Step q: barrier q, publish phase q+1 (loaded kStages steps ago) into
     // its slot, load phase q+1+kStages into the registers it freed.  Phase
     // i lives in stage i % kStages; steps are unrolled kStages at a time.
-    auto step = [&](auto ic, int q, bool more) {
+    auto step = [&](auto ic, int q, bool more) __attribute__((always_inline)) {
       constexpr int I = decltype(ic)::value;     // q % kStages
       constexpr int st = (I + 1) % kStages;
       lds_barrier();
       store_phase(q + 1, stage[st]);
       if (more) load_phase_cached(q + 1 + kStages, stage[st]);
     };
-    auto group = [&](int q, auto all_in_range) {
-      auto one = [&](auto ic) {
+    auto group = [&](int q, auto all_in_range) __attribute__((always_inline)) {
+      auto one = [&](auto ic) __attribute__((always_inline)) {
         constexpr int I = decltype(ic)::value;
         if constexpr (decltype(all_in_range)::value) {
           step(ic, q + I, true);
@@ -691,7 +695,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   constexpr int kAhead = 8;
   constexpr int kAhead8 = 6;
 
-  auto k_phase = [&](int key0) {
+  auto k_phase = [&](int key0) __attribute__((always_inline)) {
     uint32_t kb = kfrag;
     asm volatile("" : "+v"(kb));   // addresses formed here, not hoisted and kept live
     floatx4 st[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -802,7 +806,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
                     (int)pack_bf16x2(sv[2 * s + 1][2], sv[2 * s + 1][3])};
   };
 
-  auto v_phase = [&]() {
+  auto v_phase = [&]() __attribute__((always_inline)) {
     if constexpr (kV8) {
       intx4 raw[kD / 16];
 #pragma unroll
