@@ -8,6 +8,7 @@ from .binding import (
     mfa_decode_attention_gqa,
     mfa_decode_attention_mtp,
     mfa_decode_attention_phase,
+    mfa_decode_attention_noalloc,
     mfa_decode_plan_splits,
     mfa_decode_workspace_size,
     mfa_kv_append,
@@ -23,6 +24,7 @@ __all__ = [
     "mfa_decode_attention_gqa",
     "mfa_decode_attention_mtp",
     "mfa_decode_attention_phase",
+    "mfa_decode_attention_noalloc",
     "mfa_decode_plan_splits",
     "mfa_decode_workspace_size",
     "mfa_kv_append",

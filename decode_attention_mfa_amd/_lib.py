@@ -22,6 +22,7 @@ EXPORTED = (
     "mfa_decode_attention_gqa",
     "mfa_decode_attention_mtp",
     "mfa_decode_attention_phase",
+    "mfa_decode_attention_noalloc",
     "mfa_decode_workspace_size",
     "mfa_decode_mtp_workspace_size",
     "mfa_decode_plan_splits",
@@ -117,6 +118,8 @@ def load():
     lib.mfa_decode_attention_phase.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float, P,
                                                ctypes.c_size_t, ctypes.c_int32, P]
     lib.mfa_decode_attention_phase.restype = ctypes.c_int
+    lib.mfa_decode_attention_noalloc.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float, P]
+    lib.mfa_decode_attention_noalloc.restype = ctypes.c_int
     lib.mfa_decode_attention_mtp.argtypes = [desc_p, ctypes.c_int32, P, P, P, P, P, P, P, P,
                                              ctypes.c_float, P, ctypes.c_size_t, P]
     lib.mfa_decode_attention_mtp.restype = ctypes.c_int

@@ -133,6 +133,20 @@ def mfa_decode_attention(q, k_cache, v_cache, block_table, ctx_lens, out, scale,
                    v_scale, 0, num_splits, workspace, stream)
 
 
+def mfa_decode_attention_noalloc(q, k_cache, v_cache, block_table, ctx_lens, out, scale, *,
+                                 k_scale=None, v_scale=None, num_splits=0, stream=None):
+    """mfa_decode_attention with the library's own per-GPU scratch instead of a
+    workspace (no allocation anywhere in the call); see
+    mfa_decode_attention_noalloc in the header."""
+    lib = _lib.load()
+    _, desc_ref, _ = _plan(q, k_cache, block_table, out, num_splits, 0)
+    check(lib.mfa_decode_attention_noalloc(desc_ref, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(block_table), _ptr(ctx_lens), _ptr(k_scale),
+                                           _ptr(v_scale), _ptr(out), ctypes.c_float(scale),
+                                           _stream(q, stream)))
+    return out
+
+
 def mfa_decode_attention_phase(q, k_cache, v_cache, block_table, ctx_lens, out, scale, phase, *,
                                k_scale=None, v_scale=None, num_splits=0, workspace=None,
                                stream=None):

@@ -175,6 +175,19 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
 
 }  // namespace
 
+namespace mfa {
+// The MQA decode call of mfa_decode_attention, for the library's other entry
+// points (the allocation-free variant in noalloc.hip).
+mfa_status decode_mqa_entry(const mfa_decode_desc* desc, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* ctx_lens, const float* k_scale, const float* v_scale,
+                            void* out, float scale, void* workspace, size_t workspace_bytes,
+                            mfa_stream_t stream) {
+  return decode_impl(desc, 1, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
+                     scale, 0, workspace, workspace_bytes, stream, /*mqa_entry=*/true);
+}
+}  // namespace mfa
+
 extern "C" {
 
 mfa_status mfa_decode_attention(const mfa_decode_desc* desc, const void* q, const void* k_cache,

@@ -172,6 +172,29 @@ mfa_status mfa_decode_attention_phase(const mfa_decode_desc* desc, const void* q
                                       int32_t phase, mfa_stream_t stream);
 
 /*
+ * mfa_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the split partials in
+ * a library-owned device array of MFA_NOALLOC_SCRATCH_BYTES per GPU instead
+ * of a caller workspace.  The call allocates and frees nothing.  Arguments as
+ * mfa_decode_attention, less the workspace.  Returns MFA_ERR_WORKSPACE when
+ * the call would need more than the array (mfa_decode_workspace_size(desc,
+ * 0) > MFA_NOALLOC_SCRATCH_BYTES; e.g. forced split counts on large
+ * batches), and MFA_ERR_LAUNCH if the array's device address cannot be
+ * obtained.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (several streams, several host threads) race and must
+ * be serialised by the caller.  The array holds the last call's partials
+ * until the process ends; no call needs it cleared.
+ */
+#define MFA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+mfa_status mfa_decode_attention_noalloc(const mfa_decode_desc* desc, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table, const int32_t* ctx_lens,
+                                        const float* k_scale, const float* v_scale, void* out,
+                                        float scale, mfa_stream_t stream);
+
+/*
  * Multi-token queries per slot (MTP / speculative verification, "Step-3 is
  * Large yet Affordable", section 5.2: MTP raises the attention's arithmetic
  * intensity).  Each cached sequence b has num_query_tokens = Tq new query
