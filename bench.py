@@ -113,27 +113,29 @@ def source_digest():
 
 
 # Committed rocprofv3 counter summaries, by --config.
-COUNTER_SUMMARIES = {2: "mqa_decode_b64_l4096_bf16_counters.txt"}
+COUNTER_SUMMARIES = {2: "mqa_decode_b64_l4096_bf16_counters.txt",
+                     4: "mqa_decode_b256_l4096_fp8_counters.txt"}
 
 
-def committed_traffic(config):
-    """HBM bytes per call from the committed rocprofv3 counter summary of this
-    workload, or None when there is none or the kernels changed since."""
+def committed_counters(config):
+    """(HBM bytes per call, MFMA utilisation of the attention kernel) from the
+    committed rocprofv3 counter summary of this workload; (None, None) when
+    there is none or the kernels changed since it was taken."""
     name = COUNTER_SUMMARIES.get(config)
     path = os.path.join(ROOT, "profiles", name) if name else ""
     if not name or not os.path.exists(path):
-        return None
+        return None, None
     fields = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     if fields.get("source_digest") != source_digest():
-        return None
+        return None, None
     try:
-        return float(fields["traffic_bytes_per_call"])
+        return float(fields["traffic_bytes_per_call"]), float(fields["mfma_util"])
     except (KeyError, ValueError):
-        return None
+        return None, None
 
 
 def copy_calibration(steps):
@@ -519,6 +521,7 @@ def main():
     splits = mfa.mfa_decode_plan_splits(desc, window,
                                         torch.cuda.get_device_properties(dev).multi_processor_count)
 
+    counters = committed_counters(args.config) if not args.with_append else (None, None)
     res = {
         "metric": METRIC,
         "value": case.batch * tq / (ms_per_step * 1e-3),
@@ -557,7 +560,10 @@ def main():
                      "frac": (kernel_achieved or achieved) / HBM_PEAK_GBPS,
                      "kernel_us": kernel_ms * 1e3 if kernel_ms else None,
                      "step_achieved": achieved, "step_frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": committed_traffic(args.config) if tq == 1 else None,
+                     "traffic": counters[0] if tq == 1 else None,
+                     "mfma_util": counters[1] if tq == 1 else None,
+                     "counters": (f"profiles/{COUNTER_SUMMARIES[args.config]}"
+                                  if tq == 1 and counters[0] is not None else None),
                      "timed": ("the attention kernel: one HIP event pair on the launch stream "
                                "around K back-to-back launches of the call's attention phase "
                                "(no merge, no marker between launches); step_*: one event pair "
