@@ -25,6 +25,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn query tokens/s + achieved HBM GB/s (% peak), MFA 4K ctx, batch 64"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 PAGE = 64
 
 
@@ -36,7 +37,9 @@ WORKLOADS = {
     2: "MFA decode: B=64, every context 4096, 64 q heads / 1 KV head, d=256, bf16 q/K/V, "
        "paged 64-token blocks, shuffled pool",
     3: "MFA decode: B=128 ragged (prefill U[1024,8192] + Geo(1/1024) decode index), bf16, paged",
-    4: "MFA decode: B=256, context 4096, FP8 E4M3 K/V with per-head scales, bf16 q, paged",
+    4: "MFA decode from the hidden state: B=256, low-rank query path (x [256, 7168] -> 2048 -> "
+       "RMSNorm -> 64 x 256, bf16 weights) into attention over context 4096, FP8 E4M3 K/V with "
+       "per-head scales, paged",
     5: "GQA 64/4/192 decode: B=32, context 32768, dense global layer, bf16, paged",
     6: "GQA 64/4/192 decode: B=32, context 32768, 512-token sliding window, bf16, paged",
 }
@@ -56,27 +59,31 @@ def make_case(config):
     raise SystemExit(f"unknown --config {config}")
 
 
-def cpu_baseline(case, budget_s, single_thread_s=0.0):
+def cpu_baseline(case, budget_s, single_thread_s=0.0, qi=None):
     """The oracle as it stands, on the host cores: it evaluates the slots of
     the same workload one after another (cycling through the batch) until
     about budget_s seconds have passed; one slot evaluation is one query
-    token's decode-attention step.  A second, shorter run limits the BLAS
-    pool to one thread."""
+    token's decode step (with qi, the query inputs of config 4, the oracle's
+    query path first, its exact query then feeding the attention).  A
+    second, shorter run limits the BLAS pool to one thread."""
     from threadpoolctl import threadpool_info, threadpool_limits
-    from oracle import decode_attention
-    q = case.q
-    if q is None:   # FP8 config: q comes from the query path; time attention on a drawn q
-        from workloads import bf16_round_bits
-        rng = np.random.default_rng(404)
-        q = bf16_round_bits(rng.standard_normal((case.batch, case.hq, case.d), dtype=np.float32))
+    from oracle import decode_attention, query_proj
     kw = case.oracle_kwargs()
+    q = case.q
+    if qi is not None:
+        q = np.zeros((case.batch, case.hq, case.d))
+        kw["q_format"] = "f64"
 
     def run(seconds):
         done = 0
         t0 = time.perf_counter()
         while (time.perf_counter() - t0) < seconds:
+            b = done % case.batch
+            if qi is not None:
+                q[b] = query_proj(qi.x[b:b + 1], qi.w_down, qi.w_up, fmt="bf16", eps=qi.eps,
+                                  num_heads=case.hq, head_dim=case.d)[0]
             decode_attention(q, case.k_cache, case.v_cache, case.ctx_lens, case.scale,
-                             slots=[done % case.batch], **kw)
+                             slots=[b], **kw)
             done += 1
         return done, time.perf_counter() - t0
 
@@ -349,11 +356,24 @@ def main():
     else:
         t = to_device(case, device=dev)
         cpu_case = case
-    if t["q"] is None:   # FP8 config without the query path: draw q (bf16) on the host
-        from workloads import bf16_round_bits
-        rng = np.random.default_rng(404)
-        qh = bf16_round_bits(rng.standard_normal((case.batch, case.hq, case.d), dtype=np.float32))
-        t["q"] = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
+    qpath = None
+    if t["q"] is None:
+        # Config 4: the step starts from the hidden state.  The low-rank query
+        # path (x [B, 7168] -> W_qdown -> RMSNorm -> W_qup -> 64 x 256) writes
+        # the bf16 queries the FP8-cache attention then reads.
+        from workloads import config_query_inputs
+        qi = config_query_inputs(4, batch=case.batch)
+
+        def dev_bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        qpath = {"x": dev_bf16(qi.x), "wd": dev_bf16(qi.w_down.T), "wu": dev_bf16(qi.w_up.T),
+                 "eps": qi.eps, "hidden": qi.x.shape[1], "rank": qi.w_down.shape[1]}
+        t["q"] = torch.empty((case.batch, case.hq, case.d), dtype=torch.bfloat16, device=dev)
+
+    def query_path():
+        mfa.mfa_query_proj(qpath["x"], qpath["wd"], qpath["wu"], t["q"].view(case.batch, -1),
+                           num_heads=case.hq, eps=qpath["eps"])
     pools = [(t["k"], t["v"])]
     for _ in range(max(0, args.pools - 1)):
         pools.append((t["k"].clone(), t["v"].clone()))
@@ -386,6 +406,8 @@ def main():
 
     def call(i):
         k, v = pools[i % len(pools)]
+        if qpath is not None:
+            query_path()
         if args.with_append:
             mfa.mfa_kv_append(new_kv[0], new_kv[1], k, v, t["table"], t["lens"],
                               k_scale=t["k_scale"], v_scale=t["v_scale"])
@@ -491,6 +513,48 @@ def main():
         torch.cuda.synchronize()
         kernel_ms = e0.elapsed_time(e1) / args.steps
 
+    # The query path alone (config 4): K back-to-back calls under one event
+    # pair, against its own roofline max(bytes / HBM peak, FLOPs / bf16 MFMA
+    # peak) ("Step-3 is Large yet Affordable", section 4: the cost model's
+    # max form).
+    qpath_res = None
+    if qpath is not None:
+        for _ in range(args.warmup):
+            query_path()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            query_path()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qp_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        qp_bytes, qp_flops = accounting.query_proj_work(case.batch, hidden=qpath["hidden"],
+                                                        rank=qpath["rank"], heads=case.hq,
+                                                        head_dim=case.d)
+        floor_us = max(qp_bytes / (HBM_PEAK_GBPS * 1e3), qp_flops / (MFMA_BF16_PEAK_TFLOPS * 1e6))
+        qpath_res = {"us": qp_us, "bytes": qp_bytes, "flops": qp_flops, "floor_us": floor_us,
+                     "frac_of_floor": floor_us / qp_us,
+                     "achieved_GBps": qp_bytes / qp_us * 1e-3,
+                     "achieved_TFLOPs": qp_flops / qp_us * 1e-6,
+                     "timed": "one HIP event pair around K back-to-back query-path calls"}
+        # Context only: the vendor BLAS (torch.matmul -> hipBLASLt) on the same
+        # two products and layouts, timed the same way.
+        r_ctx = torch.ones(case.batch, qpath["rank"], dtype=torch.bfloat16, device="cuda")
+        lib_us = {}
+        for name, fn in (("down", lambda: torch.matmul(qpath["x"], qpath["wd"].t())),
+                         ("up", lambda: torch.matmul(r_ctx, qpath["wu"].t()))):
+            for _ in range(args.warmup):
+                fn()
+            cur = torch.cuda.current_stream()
+            e0.record(cur)
+            for _ in range(args.steps):
+                fn()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            lib_us[name] = e0.elapsed_time(e1) * 1e3 / args.steps
+        qpath_res["vendor_blas_gemm_us"] = lib_us
+
     fmt_kv = case.kv_format
     append_bytes = 0
     if args.with_append:
@@ -522,6 +586,10 @@ def main():
                                         torch.cuda.get_device_properties(dev).multi_processor_count)
 
     counters = committed_counters(args.config) if not args.with_append else (None, None)
+    if qpath is not None:
+        nbytes += qpath_res["bytes"]
+        flops += qpath_res["flops"]
+        achieved = nbytes / (call_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": case.batch * tq / (ms_per_step * 1e-3),
@@ -573,10 +641,13 @@ def main():
                               "merge kernel per step" + (", after the KV append)" if
                                                         args.with_append else ")"))},
     }
+    if qpath_res is not None:
+        res["query_path"] = qpath_res
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample of the same workload")
         res["cpu_baseline"] = cpu_baseline(cpu_case, args.cpu_seconds,
-                                           single_thread_s=args.cpu_seconds / 2)
+                                           single_thread_s=args.cpu_seconds / 2,
+                                           qi=qi if qpath is not None else None)
     print(json.dumps(res), flush=True)
 
 

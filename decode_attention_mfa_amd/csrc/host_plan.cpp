@@ -168,13 +168,13 @@ QueryProjPlan plan_query_proj(const mfa_query_proj_desc* d) {
   // Split the hidden (K) dimension of the down projection so that it fills
   // the device even at small batch; chunks stay multiples of 64.
   const int64_t kchunks = d->hidden / 64;
-  int64_t ks = std::min<int64_t>(8, kchunks);
+  int64_t ks = std::min<int64_t>(kMaxQueryKSplits, kchunks);
   while (kchunks % ks) --ks;
   pl.k_splits = (int32_t)ks;
   pl.y_partial_offset = 0;
   const size_t ybytes = (size_t)ks * d->batch * d->rank * sizeof(float);
   pl.r_offset = align_up(ybytes, kWorkspaceAlign);
-  pl.workspace_bytes = align_up(pl.r_offset + (size_t)2 * d->batch * d->rank * 2, kWorkspaceAlign);
+  pl.workspace_bytes = align_up(pl.r_offset + (size_t)d->batch * d->rank * 2, kWorkspaceAlign);
   return pl;
 }
 

@@ -76,10 +76,14 @@ mfa_status validate_kv_append(const mfa_kv_append_desc* d, const void* k_new, co
                               const void* k_cache, const void* v_cache, const int32_t* ctx_lens,
                               const float* k_scale, const float* v_scale);
 
+// Upper bound of the down projection's split-K factor (the norm kernel sums
+// at most this many partials per element).
+constexpr int kMaxQueryKSplits = 8;
+
 struct QueryProjPlan {
   int32_t k_splits;        // split-K factor of the down projection
   size_t y_partial_offset; // fp32 [k_splits, batch, rank]
-  size_t r_offset;         // bf16 hi/lo [2, batch, rank]
+  size_t r_offset;         // bf16 [batch, rank]
   size_t workspace_bytes;
 };
 

@@ -57,3 +57,19 @@ def test_window_counts_only_attended_keys_and_touched_pages():
     assert acc.pages_touched(32769, 512) == 9          # straddles a page
     assert acc.pages_touched(100, 512) == 2
     assert acc.pages_touched(0) == 0
+
+
+def test_query_path_work_against_the_linear_column():
+    # Table 2's linear column counts every projection of a layer per token; the
+    # query path (two products, 7168 -> 2048 -> 64 x 256) is most of it.  With
+    # the K, V and output projections of Table 1's shape added back it must
+    # reproduce the printed figure, and at batch 256 the path moves the bf16
+    # weights once plus x and q.
+    g = GOLD["step3_table2_linear_8k"]
+    q_bytes, q_flops = acc.query_proj_work(1)
+    kv_o_flops = 2 * (2 * 7168 * 256 + 64 * 256 * 7168)
+    total = g["layers"] * (q_flops + kv_o_flops)
+    assert abs(total - g["linear_flops"]) / g["linear_flops"] < 0.005
+    nbytes, flops = acc.query_proj_work(256)
+    assert flops == 2 * 256 * (7168 * 2048 + 2048 * 16384)
+    assert nbytes == 2 * (7168 * 2048 + 2048 * 16384) + 2 * 256 * (7168 + 16384)

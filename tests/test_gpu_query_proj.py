@@ -15,9 +15,11 @@ from gpu_helpers import TOL, assert_parity
 
 pytestmark = pytest.mark.gpu
 
-# fp32 output: bf16 inputs are exact, the products accumulate in fp32 and the
-# normalised bottleneck is carried as a bf16 hi/lo pair (~16 mantissa bits).
-TOL_F32 = (1e-3, 1e-4)
+# fp32 output: bf16 inputs are exact and the products accumulate in fp32, but
+# the normalised bottleneck is rounded once to bf16 before the up projection
+# (unit roundoff 2^-8, so q's relative-L2 error is about 1.5e-3): the same bar
+# as a bf16 output.
+TOL_F32 = TOL["bf16"]
 
 
 def _bf16(bits, dev):
