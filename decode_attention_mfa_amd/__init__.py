@@ -16,6 +16,8 @@ from .binding import (
     mfa_sparse_attention,
     mfa_sparse_select,
     mfa_sparse_summarize,
+    mfa_sparse_summarize_new,
+    V_LAYOUTS,
 )
 
 __all__ = [
@@ -32,4 +34,6 @@ __all__ = [
     "mfa_sparse_attention",
     "mfa_sparse_select",
     "mfa_sparse_summarize",
+    "mfa_sparse_summarize_new",
+    "V_LAYOUTS",
 ]

@@ -20,6 +20,7 @@ MFA_F32, MFA_BF16, MFA_FP8_E4M3 = 0, 1, 2
 EXPORTED = (
     "mfa_decode_attention",
     "mfa_decode_attention_gqa",
+    "mfa_decode_attention_gqa_layout",
     "mfa_decode_attention_mtp",
     "mfa_decode_attention_phase",
     "mfa_decode_attention_noalloc",
@@ -27,9 +28,11 @@ EXPORTED = (
     "mfa_decode_mtp_workspace_size",
     "mfa_decode_plan_splits",
     "mfa_kv_append",
+    "mfa_kv_append_layout",
     "mfa_query_proj",
     "mfa_query_proj_workspace_size",
     "mfa_sparse_summarize",
+    "mfa_sparse_summarize_new",
     "mfa_sparse_select",
     "mfa_sparse_attention",
     "mfa_sparse_workspace_size",
@@ -115,6 +118,10 @@ def load():
     lib.mfa_decode_attention_gqa.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float,
                                              ctypes.c_int32, P, ctypes.c_size_t, P]
     lib.mfa_decode_attention_gqa.restype = ctypes.c_int
+    lib.mfa_decode_attention_gqa_layout.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                                    ctypes.c_int32, ctypes.c_int32, P,
+                                                    ctypes.c_size_t, P]
+    lib.mfa_decode_attention_gqa_layout.restype = ctypes.c_int
     lib.mfa_decode_attention_phase.argtypes = [desc_p, P, P, P, P, P, P, P, P, ctypes.c_float, P,
                                                ctypes.c_size_t, ctypes.c_int32, P]
     lib.mfa_decode_attention_phase.restype = ctypes.c_int
@@ -131,6 +138,9 @@ def load():
     lib.mfa_decode_plan_splits.restype = ctypes.c_int32
     lib.mfa_kv_append.argtypes = [ctypes.POINTER(MfaKvAppendDesc), P, P, P, P, P, P, P, P, P, P]
     lib.mfa_kv_append.restype = ctypes.c_int
+    lib.mfa_kv_append_layout.argtypes = [ctypes.POINTER(MfaKvAppendDesc), P, P, P, P, P, P, P, P,
+                                         P, ctypes.c_int32, P]
+    lib.mfa_kv_append_layout.restype = ctypes.c_int
     lib.mfa_query_proj.argtypes = [qp_p, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.mfa_query_proj.restype = ctypes.c_int
     lib.mfa_query_proj_workspace_size.argtypes = [qp_p]
@@ -138,6 +148,8 @@ def load():
     sp_p = ctypes.POINTER(MfaSparseDesc)
     lib.mfa_sparse_summarize.argtypes = [sp_p, P, P, P, P, P]
     lib.mfa_sparse_summarize.restype = ctypes.c_int
+    lib.mfa_sparse_summarize_new.argtypes = [sp_p, P, P, P, ctypes.c_int32, P, P]
+    lib.mfa_sparse_summarize_new.restype = ctypes.c_int
     lib.mfa_sparse_select.argtypes = [sp_p, P, P, P, P, P, P, ctypes.c_void_p, ctypes.c_size_t, P]
     lib.mfa_sparse_select.restype = ctypes.c_int
     lib.mfa_sparse_attention.argtypes = [sp_p, P, P, P, P, P, P, P, P, ctypes.c_float, P,

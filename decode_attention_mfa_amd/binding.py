@@ -108,14 +108,41 @@ def _plan(q, k_cache, block_table, out, num_splits, window):
     return plan
 
 
+# V pool layouts (mfa_v_layout in the header).
+V_LAYOUTS = {"channel": 0, "subblock8": 1}
+
+
+def _v_layout_code(v_layout, k_cache, v_cache, block_table):
+    """The mfa_v_layout code of a layout name, after checking that v_cache has
+    that layout's shape for the K pool it comes with."""
+    if v_layout not in V_LAYOUTS:
+        raise ValueError(f"v_layout must be one of {sorted(V_LAYOUTS)}, not {v_layout!r}")
+    if v_layout == "subblock8":
+        if block_table is not None:
+            nb, hkv, _, d = k_cache.shape
+            want = (nb, hkv, PAGE // 8, d, 8)
+        else:
+            B, cap, hkv, d = k_cache.shape
+            want = (B, hkv, cap // 8, d, 8)
+        if tuple(v_cache.shape) != want:
+            raise ValueError(f"a sub-blocked V pool must have shape {want}, "
+                             f"not {tuple(v_cache.shape)}")
+    return V_LAYOUTS[v_layout]
+
+
 def _decode(entry, q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_scale, v_scale,
-            window, num_splits, workspace, stream):
+            window, num_splits, workspace, stream, v_layout="channel"):
     lib = _lib.load()
+    layout = _v_layout_code(v_layout, k_cache, v_cache, block_table)
     _, desc_ref, need = _plan(q, k_cache, block_table, out, num_splits, window)
     ws, ws_bytes = _workspace(q.device, need, workspace, "decode")
     args = [desc_ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
             _ptr(ctx_lens), _ptr(k_scale), _ptr(v_scale), _ptr(out), ctypes.c_float(scale)]
-    if entry == "gqa":
+    if entry == "gqa" and layout != V_LAYOUTS["channel"]:
+        status = lib.mfa_decode_attention_gqa_layout(*args, ctypes.c_int32(int(window)),
+                                                     ctypes.c_int32(layout), _ptr(ws),
+                                                     ctypes.c_size_t(ws_bytes), _stream(q, stream))
+    elif entry == "gqa":
         args.append(ctypes.c_int32(int(window)))
         status = lib.mfa_decode_attention_gqa(*args, _ptr(ws), ctypes.c_size_t(ws_bytes),
                                               _stream(q, stream))
@@ -165,10 +192,11 @@ def mfa_decode_attention_phase(q, k_cache, v_cache, block_table, ctx_lens, out, 
 
 def mfa_decode_attention_gqa(q, k_cache, v_cache, block_table, ctx_lens, out, scale, *,
                              window=0, k_scale=None, v_scale=None, num_splits=0, workspace=None,
-                             stream=None):
-    """GQA / sliding-window decode attention; see mfa_decode_attention_gqa."""
+                             stream=None, v_layout="channel"):
+    """GQA / sliding-window decode attention; see mfa_decode_attention_gqa (and
+    mfa_decode_attention_gqa_layout for v_layout="subblock8")."""
     return _decode("gqa", q, k_cache, v_cache, block_table, ctx_lens, out, scale, k_scale,
-                   v_scale, window, num_splits, workspace, stream)
+                   v_scale, window, num_splits, workspace, stream, v_layout)
 
 
 def mfa_decode_mtp_workspace_size(desc, num_query_tokens):
@@ -218,14 +246,18 @@ def kv_append_desc(k_new, k_cache, block_table):
 
 
 def mfa_kv_append(k_new, v_new, k_cache, v_cache, block_table, ctx_lens, *, k_scale=None,
-                  v_scale=None, active=None, stream=None):
+                  v_scale=None, active=None, stream=None, v_layout="channel"):
     """Append one token's K/V per slot and advance ctx_lens on the device; see
-    mfa_kv_append in the header."""
+    mfa_kv_append (and mfa_kv_append_layout for v_layout="subblock8")."""
     lib = _lib.load()
+    layout = _v_layout_code(v_layout, k_cache, v_cache, block_table)
     desc = kv_append_desc(k_new, k_cache, block_table)
-    check(lib.mfa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-                            _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(k_scale),
-                            _ptr(v_scale), _ptr(active), _stream(k_new, stream)))
+    args = [ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), _ptr(ctx_lens), _ptr(k_scale), _ptr(v_scale), _ptr(active)]
+    if layout != V_LAYOUTS["channel"]:
+        check(lib.mfa_kv_append_layout(*args, ctypes.c_int32(layout), _stream(k_new, stream)))
+    else:
+        check(lib.mfa_kv_append(*args, _stream(k_new, stream)))
 
 
 def sparse_desc(batch, block_table, k_cache, out, num_splits=0):
@@ -241,6 +273,18 @@ def mfa_sparse_summarize(k_idx, z, ctx_lens, summaries, *, block_table, stream=N
     desc = sparse_desc(k_idx.shape[0], block_table, None, None)
     check(lib.mfa_sparse_summarize(ctypes.byref(desc), _ptr(k_idx), _ptr(z), _ptr(ctx_lens),
                                    _ptr(summaries), _stream(k_idx, stream)))
+    return summaries
+
+
+def mfa_sparse_summarize_new(k_idx, z, ctx_lens, summaries, new_tokens, *, block_table,
+                             stream=None):
+    """Summaries of only the blocks the last new_tokens tokens completed; see
+    mfa_sparse_summarize_new."""
+    lib = _lib.load()
+    desc = sparse_desc(k_idx.shape[0], block_table, None, None)
+    check(lib.mfa_sparse_summarize_new(ctypes.byref(desc), _ptr(k_idx), _ptr(z), _ptr(ctx_lens),
+                                       ctypes.c_int32(int(new_tokens)), _ptr(summaries),
+                                       _stream(k_idx, stream)))
     return summaries
 
 

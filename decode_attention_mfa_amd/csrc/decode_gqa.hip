@@ -4,6 +4,11 @@
 // floor(h / 16); local layers attend to a 512-token window that includes the
 // current token; the dense global layer attends to everything).
 //
+// V is read channel-major ([d][64] per block) or in 8-token sub-blocks
+// ([8][d][8] per block, the layout of the sparse global attention, so that
+// one cache serves both calls); either way a 16-byte run holds 8 keys of one
+// channel, which is all the V^T tile copy needs.
+//
 // Workgroup = 4 waves = one (slot, KV group, split).  The split's keys are
 // streamed in 64-key tiles through the same LDS phase ring as the MQA kernel
 // (phase 2t = K tile [64][d], phase 2t+1 = V^T tile [d][64], 16-byte
@@ -134,7 +139,7 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
       vt = vpool + blk * p.v_block_stride + (int64_t)g * p.v_head_stride;
     } else {
       kt = kpool + ((int64_t)b * p.max_blocks + tile) * p.k_block_stride + (int64_t)g * p.k_head_stride;
-      vt = vpool + (int64_t)b * p.v_seq_stride + (int64_t)g * p.v_head_stride + (int64_t)tile * kPage;
+      vt = vpool + (int64_t)b * p.v_seq_stride + (int64_t)g * p.v_head_stride + (int64_t)tile * p.v_tile_stride;
     }
     if ((ph & 1) == 0) {
       // K tile: 64 rows of D/8 chunks; copy i covers 1 KB = 64 chunks.
@@ -147,13 +152,15 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
         dma16(kt + row * p.k_row_stride + ch * 8, dst + i * 1024);
       }
     } else {
-      // V^T tile: D rows of 8 chunks (64 keys); copy i covers 8 rows.
+      // V^T tile: D rows of 8 chunks (64 keys); copy i covers 8 rows.  Chunk
+      // ch of row (channel) `row` is keys 8ch .. 8ch + 7 of that channel,
+      // wherever the layout keeps them (channel-major or 8-token sub-blocks).
 #pragma unroll
       for (int k = 0; k < C::kDmaPerWave; ++k) {
         const int i = wave * C::kDmaPerWave + k;
         const int row = 8 * i + (lane >> 3);
         const int ch = (lane & 7) ^ swz_v(row);
-        dma16(vt + row * p.v_row_stride + ch * 8, dst + i * 1024);
+        dma16(vt + row * p.v_row_stride + ch * p.v_chunk_stride, dst + i * 1024);
       }
     }
   };

@@ -14,7 +14,10 @@ constexpr int kPage = 64;          // tokens per cache block (one kernel tile)
 //             v + block * v_block_stride + g * v_head_stride
 // with block = block_table[b * max_blocks + t]; for a contiguous cache the
 // block index is replaced by (b * max_blocks + t) for K and the V tile starts
-// at v + b * v_seq_stride + g * v_head_stride + t * 64.
+// at v + b * v_seq_stride + g * v_head_stride + t * v_tile_stride.  Inside a
+// V tile, keys 8c .. 8c + 7 of channel ch (16 contiguous bytes in bf16) start
+// at ch * v_row_stride + c * v_chunk_stride: (64, 8) for channel-major
+// blocks [d][64], (8, 8 d) for blocks cut into 8-token sub-blocks [8][d][8].
 // Query slot s holds tps consecutive query tokens of cached sequence
 // s / (tq / tps) (block-table row, length, contiguous cache slot).  With
 // tq > 1 the tq tokens are the last tq cached keys of their sequence and
@@ -57,6 +60,8 @@ struct DecodeParams {
   int64_t v_head_stride;
   int64_t v_row_stride;       // elements between consecutive channels
   int64_t v_seq_stride;       // contiguous V: elements between slots
+  int64_t v_chunk_stride;     // elements between consecutive 8-key runs of a channel
+  int64_t v_tile_stride;      // contiguous V: elements between consecutive 64-key tiles
 };
 
 // One KV-append launch (layouts as for DecodeParams with block_table set,
@@ -76,6 +81,7 @@ struct AppendParams {
   int32_t head_dim;
   int32_t max_blocks;
   int64_t num_blocks;
+  int32_t v_sub8;             // 1: V blocks cut into 8-token sub-blocks [8][d][8]
 };
 
 }  // namespace mfa

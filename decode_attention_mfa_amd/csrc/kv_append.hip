@@ -55,13 +55,17 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
   TKv* kc = static_cast<TKv*>(p.k_cache);
   TKv* vc = static_cast<TKv*>(p.v_cache);
   for (int g = 0; g < hkv; ++g) {
-    // Paged: K [blocks, Hkv, 64, d], V [blocks, Hkv, d, 64];
-    // contiguous: K [B, cap, Hkv, d], V [B, Hkv, d, cap].
+    // Paged: K [blocks, Hkv, 64, d], V [blocks, Hkv, d, 64] or, cut into
+    // 8-token sub-blocks, [blocks, Hkv, 8, d, 8];
+    // contiguous: K [B, cap, Hkv, d], V [B, Hkv, d, cap] or [B, Hkv, cap/8, d, 8].
     const int64_t k_row = p.block_table ? ((blk * hkv + g) * kPage + row) * d
                                         : (((int64_t)b * cap + pos) * hkv + g) * d;
-    const int64_t v_col = p.block_table ? (blk * hkv + g) * (int64_t)d * kPage + row
-                                        : ((int64_t)b * hkv + g) * (int64_t)d * cap + pos;
-    const int64_t v_stride = p.block_table ? kPage : cap;
+    const int tok = p.block_table ? row : pos;   // key index inside the V run
+    const int64_t v_base = p.block_table ? (blk * hkv + g) * (int64_t)d * kPage
+                                         : ((int64_t)b * hkv + g) * (int64_t)d * cap;
+    const int64_t v_col = p.v_sub8 ? v_base + (int64_t)(tok >> 3) * d * 8 + (tok & 7)
+                                   : v_base + tok;
+    const int64_t v_stride = p.v_sub8 ? 8 : (p.block_table ? kPage : cap);
     TNew kv, vv;
     if (g < kPre) {
       kv = kpre[g];

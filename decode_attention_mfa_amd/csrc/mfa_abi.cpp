@@ -45,7 +45,7 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
                               const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* ctx_lens,
                               const float* k_scale, const float* v_scale, void* out, float scale,
-                              int32_t window, void* workspace) {
+                              int32_t window, void* workspace, int32_t v_layout = 0) {
   using mfa::kPage;
   mfa::DecodeParams p{};
   p.q = q;
@@ -85,6 +85,11 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
     p.v_head_stride = hd * kPage;
     p.v_row_stride = kPage;
     p.v_seq_stride = 0;
+    p.v_chunk_stride = 8;
+    if (v_layout == MFA_V_SUBBLOCK8) {   // [blocks, Hkv, 8, d, 8]
+      p.v_row_stride = 8;
+      p.v_chunk_stride = 8 * hd;
+    }
   } else {
     const int64_t cap = (int64_t)d->max_blocks_per_seq * kPage;
     p.k_block_stride = kPage * hkv * hd;
@@ -94,6 +99,13 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
     p.v_head_stride = hd * cap;
     p.v_row_stride = cap;
     p.v_seq_stride = hkv * hd * cap;
+    p.v_chunk_stride = 8;
+    p.v_tile_stride = kPage;
+    if (v_layout == MFA_V_SUBBLOCK8) {   // [B, Hkv, cap / 8, d, 8]
+      p.v_row_stride = 8;
+      p.v_chunk_stride = 8 * hd;
+      p.v_tile_stride = kPage * hd;
+    }
   }
   return p;
 }
@@ -126,7 +138,9 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
                        const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
                        const float* k_scale, const float* v_scale, void* out, float scale,
                        int32_t window, void* workspace, size_t workspace_bytes,
-                       mfa_stream_t stream, bool mqa_entry, int phase = 0) {
+                       mfa_stream_t stream, bool mqa_entry, int phase = 0,
+                       int32_t v_layout = MFA_V_CHANNEL_MAJOR) {
+  if (v_layout != MFA_V_CHANNEL_MAJOR && v_layout != MFA_V_SUBBLOCK8) return MFA_ERR_ARG;
   mfa_decode_desc vd;
   int32_t tps = 1;
   mfa_status st = query_slot_desc(d0, tq, window, mqa_entry, &vd, &tps);
@@ -144,11 +158,13 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
     if (cus <= 0) return MFA_ERR_LAUNCH;
   }
   const mfa::DecodePlan pl = mfa::plan_decode(d, window, cus, tps);
+  // Sub-blocked V is read by the per-group bf16 path only.
+  if (v_layout == MFA_V_SUBBLOCK8 && pl.path != mfa::DecodePath::kGqaSplitKeys) return MFA_ERR_SHAPE;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return MFA_ERR_WORKSPACE;
 
   mfa::DecodeParams p = make_params(d, pl, q, k_cache, v_cache, block_table, ctx_lens, k_scale,
-                                    v_scale, out, scale, window, workspace);
+                                    v_scale, out, scale, window, workspace, v_layout);
   p.tq = tq;
   p.tps = tps;
   p.hq = d->num_q_heads * tps;   // query rows per slot
@@ -243,6 +259,18 @@ mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
                      scale, window, workspace, workspace_bytes, stream, /*mqa_entry=*/false);
 }
 
+mfa_status mfa_decode_attention_gqa_layout(const mfa_decode_desc* desc, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table, const int32_t* ctx_lens,
+                                           const float* k_scale, const float* v_scale, void* out,
+                                           float scale, int32_t window, int32_t v_layout,
+                                           void* workspace, size_t workspace_bytes,
+                                           mfa_stream_t stream) {
+  return decode_impl(desc, 1, q, k_cache, v_cache, block_table, ctx_lens, k_scale, v_scale, out,
+                     scale, window, workspace, workspace_bytes, stream, /*mqa_entry=*/false,
+                     /*phase=*/0, v_layout);
+}
+
 size_t mfa_decode_workspace_size(const mfa_decode_desc* desc, int32_t window) {
   if (mfa::validate_decode_desc(desc, window, false) != MFA_OK) return 0;
   int cus = 0;
@@ -258,13 +286,18 @@ int32_t mfa_decode_plan_splits(const mfa_decode_desc* desc, int32_t window, int3
   return mfa::plan_decode(desc, window, num_cus > 0 ? num_cus : 1).splits;
 }
 
-mfa_status mfa_kv_append(const mfa_kv_append_desc* desc, const void* k_new, const void* v_new,
-                         void* k_cache, void* v_cache, const int32_t* block_table,
-                         int32_t* ctx_lens, const float* k_scale, const float* v_scale,
-                         const int32_t* active, mfa_stream_t stream) {
+mfa_status mfa_kv_append_layout(const mfa_kv_append_desc* desc, const void* k_new,
+                                const void* v_new, void* k_cache, void* v_cache,
+                                const int32_t* block_table, int32_t* ctx_lens,
+                                const float* k_scale, const float* v_scale, const int32_t* active,
+                                int32_t v_layout, mfa_stream_t stream) {
+  if (v_layout != MFA_V_CHANNEL_MAJOR && v_layout != MFA_V_SUBBLOCK8) return MFA_ERR_ARG;
   mfa_status st = mfa::validate_kv_append(desc, k_new, v_new, k_cache, v_cache, ctx_lens, k_scale,
                                           v_scale);
-  if (st != MFA_OK || desc->batch == 0) return st;
+  if (st != MFA_OK) return st;
+  // Sub-blocked V is the bf16 layout of the per-group and sparse paths.
+  if (v_layout == MFA_V_SUBBLOCK8 && desc->kv_dtype != MFA_BF16) return MFA_ERR_DTYPE;
+  if (desc->batch == 0) return MFA_OK;
   if (block_table && desc->num_blocks <= 0) return MFA_ERR_SHAPE;   // a paged call needs a pool
   mfa::AppendParams p{};
   p.k_new = k_new;
@@ -281,9 +314,18 @@ mfa_status mfa_kv_append(const mfa_kv_append_desc* desc, const void* k_new, cons
   p.head_dim = desc->head_dim;
   p.max_blocks = desc->max_blocks_per_seq;
   p.num_blocks = desc->num_blocks;
+  p.v_sub8 = v_layout == MFA_V_SUBBLOCK8;
   const hipError_t e = mfa::launch_kv_append(p, desc->new_dtype, desc->kv_dtype,
                                              reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MFA_OK : MFA_ERR_LAUNCH;
+}
+
+mfa_status mfa_kv_append(const mfa_kv_append_desc* desc, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_table,
+                         int32_t* ctx_lens, const float* k_scale, const float* v_scale,
+                         const int32_t* active, mfa_stream_t stream) {
+  return mfa_kv_append_layout(desc, k_new, v_new, k_cache, v_cache, block_table, ctx_lens,
+                              k_scale, v_scale, active, MFA_V_CHANNEL_MAJOR, stream);
 }
 
 mfa_status mfa_query_proj(const mfa_query_proj_desc* desc, const void* x, const void* w_qdown,

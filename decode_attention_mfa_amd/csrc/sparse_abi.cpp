@@ -82,12 +82,11 @@ mfa::SparseParams base_params(const mfa_sparse_desc* d, const int32_t* ctx_lens)
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-mfa_status mfa_sparse_summarize(const mfa_sparse_desc* desc, const void* k_idx, const void* z,
-                                const int32_t* ctx_lens, uint8_t* summaries, mfa_stream_t stream) {
+// new_tokens == 0: every complete block; > 0: the blocks the last new_tokens
+// tokens of each request completed.
+mfa_status summarize(const mfa_sparse_desc* desc, const void* k_idx, const void* z,
+                     const int32_t* ctx_lens, int32_t new_tokens, uint8_t* summaries,
+                     mfa_stream_t stream) {
   const mfa_status st = validate(desc);
   if (st != MFA_OK || desc->batch == 0) return st;
   if (!k_idx || !z || !ctx_lens || !summaries) return MFA_ERR_NULL;
@@ -96,8 +95,28 @@ mfa_status mfa_sparse_summarize(const mfa_sparse_desc* desc, const void* k_idx, 
   p.k_idx = k_idx;
   p.z = z;
   p.summ_out = summaries;
+  p.new_tokens = new_tokens;
   return mfa::launch_sparse_summary(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? MFA_OK : MFA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+mfa_status mfa_sparse_summarize(const mfa_sparse_desc* desc, const void* k_idx, const void* z,
+                                const int32_t* ctx_lens, uint8_t* summaries, mfa_stream_t stream) {
+  return summarize(desc, k_idx, z, ctx_lens, 0, summaries, stream);
+}
+
+mfa_status mfa_sparse_summarize_new(const mfa_sparse_desc* desc, const void* k_idx,
+                                    const void* z, const int32_t* ctx_lens, int32_t new_tokens,
+                                    uint8_t* summaries, mfa_stream_t stream) {
+  const mfa_status st = validate(desc);
+  if (st != MFA_OK) return st;
+  if (new_tokens < 1 || (int64_t)new_tokens > (int64_t)desc->max_blocks_per_seq * 64)
+    return MFA_ERR_ARG;
+  return summarize(desc, k_idx, z, ctx_lens, new_tokens, summaries, stream);
 }
 
 mfa_status mfa_sparse_select(const mfa_sparse_desc* desc, const void* q_idx, const float* w,

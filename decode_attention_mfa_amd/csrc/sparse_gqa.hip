@@ -78,18 +78,22 @@ __device__ __forceinline__ float round_bf16(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Block summaries: grid (blocks / 4, B), thread d = coordinate.
+// 1. Block summaries: grid (blocks / 4, B), thread d = coordinate.  Blocks
+// r0 .. nb - 1 of each request, r0 = 0 (every complete block) or, with
+// new_tokens = n > 0, r0 = floor((L - n) / 8): the blocks that the last n
+// tokens completed (a decode step completes a block at its eighth token).
 __global__ void __launch_bounds__(256) sparse_summary_kernel(SparseParams p) {
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int L = slot_len(p.dp.ctx_lens[b], p.dp.max_blocks);
   const int nb = min(L / kSparseBlock, p.cap8);
+  const int r0 = p.new_tokens > 0 ? max(L - p.new_tokens, 0) / kSparseBlock : 0;
   const int64_t cap = (int64_t)p.dp.max_blocks * kPage;
   const uint16_t* kp = static_cast<const uint16_t*>(p.k_idx) + (int64_t)b * cap * kSparseWidth + d;
   const uint16_t* zp = static_cast<const uint16_t*>(p.z) + (int64_t)b * cap * kSparseWidth + d;
   uint8_t* cp = p.summ_out + (int64_t)b * p.cap8 * kSparseWidth + d;
-  const int r_end = min(nb, (int)(blockIdx.x + 1) * 4);
-  for (int r = blockIdx.x * 4; r < r_end; ++r) {
+  const int r_end = min(nb, r0 + (int)(blockIdx.x + 1) * 4);
+  for (int r = r0 + blockIdx.x * 4; r < r_end; ++r) {
     float zv[kSparseBlock], kv[kSparseBlock];
 #pragma unroll
     for (int j = 0; j < kSparseBlock; ++j) {
@@ -596,7 +600,10 @@ __global__ void __launch_bounds__(256) sparse_attention_kernel(SparseParams sp) 
 }  // namespace
 
 hipError_t launch_sparse_summary(const SparseParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.cap8 + 3) / 4), (unsigned)p.dp.batch);
+  // The last n tokens complete at most ceil(n / 8) blocks.
+  const int new_blocks = (p.new_tokens + kSparseBlock - 1) / kSparseBlock;
+  const int blocks = (p.new_tokens > 0 && new_blocks < p.cap8) ? new_blocks : p.cap8;
+  const dim3 grid((unsigned)((blocks + 3) / 4), (unsigned)p.dp.batch);
   hipLaunchKernelGGL(sparse_summary_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -33,6 +33,7 @@ struct SparseParams {
   const void* k_idx;        // [B, cap, 256] bf16 proxy keys
   const void* z;            // [B, cap, 256] bf16 compression logits
   int32_t cap8;             // summaries per request (cap / 8)
+  int32_t new_tokens;       // > 0: summarise only the blocks the last new_tokens tokens completed
   float* scores;            // [B, 4, cap8] fp32 scores (workspace)
   int32_t* sel_out;         // selection outputs
   int32_t* nsel_out;

@@ -232,6 +232,42 @@ mfa_status mfa_decode_attention_gqa(const mfa_decode_desc* desc, const void* q,
                                     float scale, int32_t window, void* workspace,
                                     size_t workspace_bytes, mfa_stream_t stream);
 
+/*
+ * Layouts of a V pool, for the entries that take a v_layout argument.
+ *   MFA_V_CHANNEL_MAJOR  paged [num_blocks, Hkv, d, 64], contiguous
+ *                        [B, Hkv, d, cap] (the layout of every other entry)
+ *   MFA_V_SUBBLOCK8      paged [num_blocks, Hkv, 8, d, 8], contiguous
+ *                        [B, Hkv, cap/8, d, 8]: token j of a 64-token block
+ *                        sits in 8-token sub-block j / 8 at column j % 8
+ *                        (the V layout of mfa_sparse_attention)
+ * Both keep the 8 tokens of one channel in 16 contiguous bytes (bf16).
+ */
+typedef enum mfa_v_layout {
+  MFA_V_CHANNEL_MAJOR = 0,
+  MFA_V_SUBBLOCK8 = 1
+} mfa_v_layout;
+
+/*
+ * mfa_decode_attention_gqa with the V pool in layout v_layout.  With
+ * MFA_V_SUBBLOCK8 one cache of the Step-5 global layer (K [num_blocks, 4, 64,
+ * 192], V [num_blocks, 4, 8, 192, 8]) serves this dense call, the sparse
+ * call mfa_sparse_attention and the append mfa_kv_append_layout: the dense
+ * global layer and the sparse path attend to the same original K/V
+ * ("Step-5-Preview: Sparse GQA, Indexer und KV-Speicher", section "Die
+ * eigentliche Attention liest weiterhin originale K/V").  The result is
+ * bit-identical to the channel-major call on the same values.
+ * MFA_V_SUBBLOCK8 is read by the per-group bf16 path only ((Hq/Hkv, d) =
+ * (16, 192) or (16, 256), bf16 cache); other shapes return MFA_ERR_SHAPE.
+ * Other v_layout values return MFA_ERR_ARG.
+ */
+mfa_status mfa_decode_attention_gqa_layout(const mfa_decode_desc* desc, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table, const int32_t* ctx_lens,
+                                           const float* k_scale, const float* v_scale, void* out,
+                                           float scale, int32_t window, int32_t v_layout,
+                                           void* workspace, size_t workspace_bytes,
+                                           mfa_stream_t stream);
+
 /* Workspace bytes a call with this descriptor and window needs (0 when every
  * slot fits one split; room for the even page partition when num_splits is 0
  * and the call may use it).  Pure host arithmetic: no HIP call is made when
@@ -308,6 +344,19 @@ mfa_status mfa_kv_append(const mfa_kv_append_desc* desc, const void* k_new, cons
                          const int32_t* active, mfa_stream_t stream);
 
 /*
+ * mfa_kv_append with the V pool in layout v_layout (mfa_v_layout): the new
+ * token's V column goes to sub-block pos % 64 / 8, column pos % 8 under
+ * MFA_V_SUBBLOCK8, which needs a BF16 cache (other dtypes return
+ * MFA_ERR_DTYPE); other v_layout values return MFA_ERR_ARG.  Values are
+ * copied bit for bit, as by mfa_kv_append.
+ */
+mfa_status mfa_kv_append_layout(const mfa_kv_append_desc* desc, const void* k_new,
+                                const void* v_new, void* k_cache, void* v_cache,
+                                const int32_t* block_table, int32_t* ctx_lens,
+                                const float* k_scale, const float* v_scale, const int32_t* active,
+                                int32_t v_layout, mfa_stream_t stream);
+
+/*
  * Low-rank MFA query path ("Step-3 is Large yet Affordable", section 2):
  *     y = x W_qdown^T;  r = y / sqrt(mean(y^2) + eps) * gain;  q = r W_qup^T
  * and q is viewed as [B, num_heads, head_dim] (head h = output columns
@@ -369,6 +418,22 @@ typedef struct mfa_sparse_desc {
  */
 mfa_status mfa_sparse_summarize(const mfa_sparse_desc* desc, const void* k_idx, const void* z,
                                 const int32_t* ctx_lens, uint8_t* summaries, mfa_stream_t stream);
+
+/*
+ * Summaries of only the blocks that the last new_tokens tokens of each
+ * request completed: blocks r with floor((L - new_tokens) / 8) <= r <
+ * floor(L / 8), L = ctx_lens[b] read on the device (so a captured graph stays
+ * valid as the lengths advance).  Each is computed exactly as by
+ * mfa_sparse_summarize; every other entry of `summaries` is left as it is.
+ * Decode summarises a block when its eighth token arrives ("Step-5-Preview:
+ * Sparse GQA, Indexer und KV-Speicher", section "Acht Tokens ergeben einen
+ * Such-Key"): a decode loop calls this with new_tokens = 1 after each
+ * append, and with Tq after appending Tq tokens.  new_tokens outside
+ * [1, max_blocks_per_seq * 64] returns MFA_ERR_ARG.
+ */
+mfa_status mfa_sparse_summarize_new(const mfa_sparse_desc* desc, const void* k_idx,
+                                    const void* z, const int32_t* ctx_lens, int32_t new_tokens,
+                                    uint8_t* summaries, mfa_stream_t stream);
 
 /*
  * Scores s[g, r] = sum_h w[g, h] ReLU(Q8(q_idx[g, h]) . c[r]) for the

@@ -254,3 +254,57 @@ def test_binding_rejects_strided_tensors_and_ragged_capacity():
     vc = torch.zeros((2, 1, 256, 100), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="multiple of 64"):
         mfa.mfa_decode_attention(q, kc, vc, None, lens, out, 0.0625, num_splits=1)
+
+
+def test_v_layout_and_incremental_summary_rules():
+    from decode_attention_mfa_amd._lib import MfaKvAppendDesc
+    lib = _lib.load()
+
+    def gqa_layout(d, layout):
+        return lib.mfa_decode_attention_gqa_layout(ctypes.byref(d), A, A, A, A, A, None, None, A,
+                                                   ctypes.c_float(0.07), ctypes.c_int32(0),
+                                                   ctypes.c_int32(layout), None,
+                                                   ctypes.c_size_t(0), None)
+    step5 = dict(num_q_heads=64, num_kv_heads=4, head_dim=192, num_splits=1)
+    assert gqa_layout(desc(**step5), 2) == MFA_ERR_ARG
+    assert gqa_layout(desc(**step5), -1) == MFA_ERR_ARG
+    # sub-blocked V is read by the per-group bf16 path only
+    assert gqa_layout(desc(num_splits=1), 1) == MFA_ERR_SHAPE                  # MQA shape
+    assert gqa_layout(desc(q_dtype=MFA_F32, kv_dtype=MFA_F32, out_dtype=MFA_F32,
+                           **step5), 1) == MFA_ERR_SHAPE                       # fp32 path
+
+    def append(kv_dtype, new_dtype, layout):
+        d = MfaKvAppendDesc(batch=4, num_kv_heads=4, head_dim=192, page_size=64,
+                            max_blocks_per_seq=8, num_blocks=64, new_dtype=new_dtype,
+                            kv_dtype=kv_dtype)
+        return lib.mfa_kv_append_layout(ctypes.byref(d), A, A, A, A, A, A, A, A, None,
+                                        ctypes.c_int32(layout), None)
+    assert append(MFA_BF16, MFA_BF16, 3) == MFA_ERR_ARG
+    assert append(MFA_F32, MFA_F32, 1) == MFA_ERR_DTYPE
+    assert append(MFA_FP8_E4M3, MFA_BF16, 1) == MFA_ERR_DTYPE
+
+    def summ_new(d, n):
+        return lib.mfa_sparse_summarize_new(ctypes.byref(d) if d is not None else None, A, A, A,
+                                            ctypes.c_int32(n), A, None)
+    assert summ_new(None, 1) == MFA_ERR_NULL
+    assert summ_new(sparse(), 0) == MFA_ERR_ARG
+    assert summ_new(sparse(), -3) == MFA_ERR_ARG
+    assert summ_new(sparse(max_blocks_per_seq=4), 4 * 64 + 1) == MFA_ERR_ARG
+    assert summ_new(sparse(batch=0), 1) == 0
+
+
+def test_binding_checks_the_sub_blocked_v_shape():
+    import torch
+    import decode_attention_mfa_amd as mfa
+    q = torch.zeros((2, 64, 192), dtype=torch.bfloat16)
+    k = torch.zeros((4, 4, 64, 192), dtype=torch.bfloat16)
+    v_channel = torch.zeros((4, 4, 192, 64), dtype=torch.bfloat16)
+    table = torch.zeros((2, 2), dtype=torch.int32)
+    lens = torch.zeros((2,), dtype=torch.int32)
+    out = torch.zeros_like(q)
+    with pytest.raises(ValueError, match="sub-blocked V pool"):
+        mfa.mfa_decode_attention_gqa(q, k, v_channel, table, lens, out, 0.07, num_splits=1,
+                                     v_layout="subblock8")
+    with pytest.raises(ValueError, match="v_layout"):
+        mfa.mfa_decode_attention_gqa(q, k, v_channel, table, lens, out, 0.07, num_splits=1,
+                                     v_layout="tokens")
