@@ -303,6 +303,9 @@ def main():
     ap.add_argument("--prewarm", type=float, default=0.3,
                     help="seconds of untimed steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--v-layout", choices=["channel", "subblock8"], default="channel",
+                    help="V pool layout of the per-group configs (5, 6): channel-major, or "
+                         "the 8-token sub-blocks the sparse global attention reads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -374,6 +377,11 @@ def main():
     def query_path():
         mfa.mfa_query_proj(qpath["x"], qpath["wd"], qpath["wu"], t["q"].view(case.batch, -1),
                            num_heads=case.hq, eps=qpath["eps"])
+    if args.v_layout != "channel":
+        if case.hkv == 1 or args.mtp != 1:
+            raise SystemExit("--v-layout subblock8 is read by the per-group configs (5, 6)")
+        nb_, hkv_, d_, page_ = t["v"].shape
+        t["v"] = t["v"].view(nb_, hkv_, d_, page_ // 8, 8).permute(0, 1, 3, 2, 4).contiguous()
     pools = [(t["k"], t["v"])]
     for _ in range(max(0, args.pools - 1)):
         pools.append((t["k"].clone(), t["v"].clone()))
@@ -422,7 +430,8 @@ def main():
         else:
             mfa.mfa_decode_attention_gqa(t["q"], k, v, t["table"], t["lens"], out, case.scale,
                                          window=window, k_scale=t["k_scale"],
-                                         v_scale=t["v_scale"], num_splits=args.num_splits)
+                                         v_scale=t["v_scale"], num_splits=args.num_splits,
+                                         v_layout=args.v_layout)
 
     # Untimed pre-warm: the GPU raises its clocks over a few hundred
     # microseconds of load, so the same step is run for args.prewarm seconds
@@ -611,7 +620,8 @@ def main():
                    "page": 64, "window": window, "splits": splits, "kv_pool_copies": len(pools),
                    "launch": "hip graph replay" if args.graph else "eager",
                    "prewarm_s": args.prewarm,
-                   "append": bool(args.with_append), "query_tokens_per_slot": tq},
+                   "append": bool(args.with_append), "query_tokens_per_slot": tq,
+                   "v_layout": args.v_layout},
         "hbm_gbps": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "call_us_mean": call_ms * 1e3,
