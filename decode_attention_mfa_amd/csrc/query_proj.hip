@@ -79,12 +79,15 @@ __device__ __forceinline__ void wait_steps(int n) {
 
 enum GemmOut : int { kPartialF32 = 0, kOutBf16 = 1, kOutF32 = 2 };
 
-// Workgroup b of a 1-D grid of `tiles`; consecutive tile numbers are kept on
-// one XCD (dispatch deals workgroups to the 8 XCDs in turn), so the M tiles
-// of one column of B share that XCD's L2.
-__device__ __forceinline__ int xcd_tile(int b, int tiles) {
-  if (tiles % 8) return b;
-  return (b % 8) * (tiles / 8) + b / 8;
+// Work item of workgroup b in a 1-D grid of n: dispatch deals workgroups to
+// the 8 XCDs in turn, so b is renumbered XCD-major and consecutive work items
+// share one XCD and its L2.  Work item i is (split i / tiles, tile i % tiles),
+// tile t = (m tile t % m_tiles, n tile t / m_tiles): with 8 splits each XCD
+// takes one k range (every operand byte is fetched from HBM once), with one
+// split the M tiles of one column of B share an XCD.
+__device__ __forceinline__ int xcd_item(int b, int n) {
+  if (n % 8) return b;
+  return (b % 8) * (n / 8) + b / 8;
 }
 
 template <int kMode>
@@ -92,10 +95,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M, int N,
     int m_tiles, int n_tiles, int k_len, void* __restrict__ C, int ldc, size_t c_split_stride) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageBytes];
-  const int t = xcd_tile((int)blockIdx.x, m_tiles * n_tiles);
+  const int tiles = m_tiles * n_tiles;
+  const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int split = item / tiles;
+  const int t = item - split * tiles;
   const int m_tile = t % m_tiles;
   const int n_tile = t / m_tiles;
-  const int split = (int)blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -295,7 +300,7 @@ mfa_status query_proj_enqueue(const mfa_query_proj_desc* d, const QueryProjPlan&
   const int m_tiles = (B + kTile - 1) / kTile;
   {
     const int n_tiles = (R + kTile - 1) / kTile;
-    dim3 grid(m_tiles * n_tiles, pl.k_splits);
+    dim3 grid(m_tiles * n_tiles * pl.k_splits);
     hipLaunchKernelGGL((gemm_kernel<kPartialF32>), grid, dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(x), H, static_cast<const uint16_t*>(w_down), H,
                        B, R, m_tiles, n_tiles, H / pl.k_splits, y_part, R, (size_t)B * R);
@@ -304,7 +309,7 @@ mfa_status query_proj_enqueue(const mfa_query_proj_desc* d, const QueryProjPlan&
                      R, d->eps, gain, r);
   {
     const int n_tiles = (N + kTile - 1) / kTile;
-    dim3 grid(m_tiles * n_tiles, 1);
+    dim3 grid(m_tiles * n_tiles);
     if (d->out_dtype == MFA_F32)
       hipLaunchKernelGGL((gemm_kernel<kOutF32>), grid, dim3(kThreads), 0, stream, r, R,
                          static_cast<const uint16_t*>(w_up), R, B, N, m_tiles, n_tiles, R, q_out, N,
