@@ -67,9 +67,17 @@ constexpr float kLazyRescale = 8.f;    // log2 headroom before the max moves
 // LDS swizzles (XOR on the 16-byte chunk index).  The 16 lanes reading one
 // K operand hold keys {0..3, 8..11, 16..19, 24..27} + const: swz_k gives
 // them 16 distinct bank quads.  A V^T read has 16 lanes on 16 consecutive
-// channels (two per 256-byte bank row).
+// channels (rows of 128 bytes) and four key chunks across q4.  With the bf16
+// key map (chunk 4s + q4) the chunk is XORed with the channel's low three
+// bits; an earlier map that also folded in channel bit 3 cost every such read
+// a 2-way bank conflict (LDS bank-conflict counter, a quarter of the kernel's
+// LDS cycles).  The 8-bit key map (chunks 2q4 + s) keeps that older map,
+// which is conflict-free for its reads.
 __device__ __forceinline__ int swz_k(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
-__device__ __forceinline__ int swz_v(int ch) { return (ch & 7) ^ ((ch >> 3) & 1); }
+template <bool kMap16>
+__device__ __forceinline__ int swz_v(int ch) {
+  return kMap16 ? (ch & 7) ^ ((ch >> 3) & 1) : (ch & 7);
+}
 // FP8 tiles (16-byte chunks of 16 codes): the 16 lanes of one K read hold
 // keys {0..3, 16..19, 32..35, 48..51} + const (rows of 256 B, one bank row
 // each); the 16 lanes of one V^T read hold 16 consecutive channels (rows of
@@ -263,7 +271,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   auto vlds = [&](int k, int c) __attribute__((always_inline)) {
     const int row = vrow0 + (kFp8 ? 64 : 32) * k;
     return kV8 ? (uint32_t)(row * 64 + ((c ^ swz_v8(vrow0)) << 4))
-               : (uint32_t)(row * 128 + ((c ^ swz_v(vrow0)) << 4));
+               : (uint32_t)(row * 128 + ((c ^ swz_v<kMap16>(vrow0)) << 4));
   };
 
   // Register-staged loads of one phase (tiles clamped into the table row:
@@ -685,8 +693,8 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   // 8-bit V^T: code chunk q4 ^ swz_v8(r) holds keys 16q4 .. +15, both
   // steps, at vfrag0 + 1024 t.
   const uint32_t vfrag0 = kV8 ? r * 64 + ((q4 ^ swz_v8(r)) << 4)
-                              : r * 128 + (((kMap16 ? 2 * q4 : q4) ^ swz_v(r)) << 4);
-  const uint32_t vfrag1 = r * 128 + (((kMap16 ? 2 * q4 + 1 : 4 + q4) ^ swz_v(r)) << 4);
+                              : r * 128 + (((kMap16 ? 2 * q4 : q4) ^ swz_v<kMap16>(r)) << 4);
+  const uint32_t vfrag1 = r * 128 + (((kMap16 ? 2 * q4 + 1 : 4 + q4) ^ swz_v<kMap16>(r)) << 4);
 
   intx4 pb[2];
   // LDS operand reads issued ahead of the products (16-byte reads; FP8 K
