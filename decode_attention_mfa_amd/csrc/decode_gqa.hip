@@ -48,12 +48,14 @@ struct GqaCfg {
   static constexpr int kChunks = D / 8;                            // 16-byte chunks per K row
 };
 
-// K rows (2D bytes): XOR the chunk index with a key-dependent value so the 16
-// lanes of one MFMA operand read 16 distinct bank quads.  d = 192 keeps the
-// XOR inside aligned groups of 8 chunks (24 chunks per row).
+// K rows (2D bytes): XOR the chunk index with a key-dependent value so that
+// the lanes of one MFMA operand read conflict-free (checked with the LDS
+// bank-conflict counter: folding key bit 3 into the d = 192 map cost every
+// K read a 2-way conflict).  d = 192 keeps the XOR inside aligned groups of
+// 8 chunks (24 chunks per row).
 template <int D>
 __device__ __forceinline__ int swz_k(int key) {
-  return D == 256 ? (key & 15) : ((key & 7) ^ ((key >> 3) & 1));
+  return D == 256 ? (key & 15) : (key & 7);
 }
 // V^T rows (128 bytes, 8 chunks).
 __device__ __forceinline__ int swz_v(int ch) { return (ch & 7) ^ ((ch >> 3) & 1); }
@@ -265,10 +267,14 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
     wave_ml[wave][r][0] = m_run;
     wave_ml[wave][r][1] = l_w;
   }
-  float* obuf = reinterpret_cast<float*>(ring);        // [4][kG][D]
+  // [4][kG][D + 4]: the 16-byte pad per head row spreads the 16 rows a
+  // store instruction touches over every bank (a row of D floats is a whole
+  // number of bank rows, which made each store a 16-way conflict).
+  constexpr int kOStride = D + 4;
+  float* obuf = reinterpret_cast<float*>(ring);
 #pragma unroll
   for (int ct = 0; ct < D / 16; ++ct)
-    *reinterpret_cast<floatx4*>(obuf + ((wave * kG + r) * D + ct * 16 + q4 * 4)) = acc[ct];
+    *reinterpret_cast<floatx4*>(obuf + ((wave * kG + r) * kOStride + ct * 16 + q4 * 4)) = acc[ct];
   __syncthreads();
 
   // Thread t: head t / 16, channels 4*(t % 16) + 64*k.
@@ -288,7 +294,7 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
   for (int c4 = (threadIdx.x & 15) * 4; c4 < D; c4 += 64) {
     floatx4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) o += wgt[w] * *reinterpret_cast<const floatx4*>(obuf + (w * kG + h) * D + c4);
+    for (int w = 0; w < 4; ++w) o += wgt[w] * *reinterpret_cast<const floatx4*>(obuf + (w * kG + h) * kOStride + c4);
     if (p.splits == 1) {
       const floatx4 v = o * (v_scale / lsum);
       const int64_t off = ((int64_t)b * p.hq + ghead) * D + c4;

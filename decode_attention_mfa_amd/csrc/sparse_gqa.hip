@@ -349,7 +349,9 @@ __global__ void __launch_bounds__(kSelThreads) sparse_select_kernel(SparseParams
 // 3. Attention over the selected blocks: one workgroup of 4 waves per
 // (request, group, split).
 
-__device__ __forceinline__ int swz_k(int key) { return (key & 7) ^ ((key >> 3) & 1); }
+// K rows of 384 bytes: XOR with the key's low three bits (inside aligned
+// groups of 8 chunks) keeps the K operand reads free of bank conflicts.
+__device__ __forceinline__ int swz_k(int key) { return key & 7; }
 __device__ __forceinline__ int swz_v(int ch) { return (ch & 7) ^ ((ch >> 3) & 1); }
 
 template <int N>
@@ -557,10 +559,14 @@ __global__ void __launch_bounds__(256) sparse_attention_kernel(SparseParams sp) 
     wave_ml[wave][r][0] = m_run;
     wave_ml[wave][r][1] = l_w;
   }
-  float* obuf = reinterpret_cast<float*>(ring);        // [4][kG][kD]
+  // [4][kG][kD + 4]: the 16-byte pad per head row spreads the 16 rows a
+  // store instruction touches over every bank (a row of kD floats is a whole
+  // number of bank rows, which made each store a 16-way conflict).
+  constexpr int kOStride = kD + 4;
+  float* obuf = reinterpret_cast<float*>(ring);
 #pragma unroll
   for (int ct = 0; ct < kD / 16; ++ct)
-    *reinterpret_cast<floatx4*>(obuf + ((wave * kG + r) * kD + ct * 16 + q4 * 4)) = acc[ct];
+    *reinterpret_cast<floatx4*>(obuf + ((wave * kG + r) * kOStride + ct * 16 + q4 * 4)) = acc[ct];
   __syncthreads();
 
   // Thread t: head t / 16, channels 4 (t % 16) + 64 k.
@@ -580,7 +586,7 @@ __global__ void __launch_bounds__(256) sparse_attention_kernel(SparseParams sp) 
   for (int c4 = (threadIdx.x & 15) * 4; c4 < kD; c4 += 64) {
     floatx4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) o += wgt[w] * *reinterpret_cast<const floatx4*>(obuf + (w * kG + h) * kD + c4);
+    for (int w = 0; w < 4; ++w) o += wgt[w] * *reinterpret_cast<const floatx4*>(obuf + (w * kG + h) * kOStride + c4);
     if (p.splits == 1) {
       const floatx4 v = o * (1.f / lsum);
       const int64_t off = ((int64_t)b * p.hq + ghead) * kD + c4;
