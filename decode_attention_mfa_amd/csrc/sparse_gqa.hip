@@ -162,10 +162,14 @@ __global__ void __launch_bounds__(256) sparse_score_kernel(SparseParams p) {
   // into LDS.  Fragments: column col = 4g + h of lane l % 16; K-step c takes
   // coordinates 64(c/2) + 16(l/16) + 8(c%2) .. +7, the channel map under
   // which one 16-byte read of codes holds two steps' A operands.
-  __shared__ __attribute__((aligned(16))) uint16_t q8s[kSparseGroups * kSparseHeads * kSparseWidth];
+  // Rows of kSparseWidth + 8 values: the 16-byte pad spreads the 16 columns a
+  // fragment read touches over every bank (unpadded rows are whole bank rows).
+  constexpr int kQ8Stride = kSparseWidth + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t q8s[kSparseGroups * kSparseHeads * kQ8Stride];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(p.q_idx) +
                          (int64_t)b * kSparseGroups * kSparseHeads * kSparseWidth + 16 * threadIdx.x;
+    uint16_t* qs = q8s + (threadIdx.x >> 4) * kQ8Stride + 16 * (threadIdx.x & 15);
     const intx4 v0 = *reinterpret_cast<const intx4*>(qp), v1 = *reinterpret_cast<const intx4*>(qp + 8);
     const int w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     int codes[4];
@@ -175,8 +179,8 @@ __global__ void __launch_bounds__(256) sparse_score_kernel(SparseParams p) {
                        ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)((uint32_t)w[2 * k] >> 16))) << 8) |
                        ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)(w[2 * k + 1] & 0xFFFF)))) << 16 |
                        ((uint32_t)e4m3fn_encode(bf16_bits_to_float((uint16_t)((uint32_t)w[2 * k + 1] >> 16))) << 24));
-    *reinterpret_cast<intx4*>(q8s + 16 * threadIdx.x) = e4m3x8_to_bf16(codes[0], codes[1]);
-    *reinterpret_cast<intx4*>(q8s + 16 * threadIdx.x + 8) = e4m3x8_to_bf16(codes[2], codes[3]);
+    *reinterpret_cast<intx4*>(qs) = e4m3x8_to_bf16(codes[0], codes[1]);
+    *reinterpret_cast<intx4*>(qs + 8) = e4m3x8_to_bf16(codes[2], codes[3]);
   }
   __syncthreads();
   const int col = lane & 15, q4 = lane >> 4;
@@ -184,7 +188,7 @@ __global__ void __launch_bounds__(256) sparse_score_kernel(SparseParams p) {
   intx4 qf[kSparseWidth / 32];
 #pragma unroll
   for (int c = 0; c < kSparseWidth / 32; ++c)
-    qf[c] = *reinterpret_cast<const intx4*>(q8s + col * kSparseWidth + 64 * (c >> 1) + 16 * q4 + 8 * (c & 1));
+    qf[c] = *reinterpret_cast<const intx4*>(q8s + col * kQ8Stride + 64 * (c >> 1) + 16 * q4 + 8 * (c & 1));
   const float wgt = p.w[(b * kSparseGroups + grp) * kSparseHeads + sh];
   if (16 * t0 >= R) return;   // this wave's tiles are past the candidates
 
