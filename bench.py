@@ -45,9 +45,10 @@ WORKLOADS = {
 }
 
 
-def make_case(config):
+def make_case(config, fp8=False):
     """Host-drawn inputs for configs 2-4; the Step-5 layer (5: global, 6: local
-    window) is drawn on the device (its 1.6 GB pool takes minutes on the host)."""
+    window) is drawn on the device (its 1.6 GB pool takes minutes on the host),
+    with an E4M3 cache (per-group scales) when fp8 is set."""
     from workloads import config_case
     if config in (2, 3, 4):
         return config_case(config, nan_tail=False)
@@ -55,7 +56,7 @@ def make_case(config):
         from workloads.device_gen import make_device_case
         return make_device_case(5, batch=32, ctx_lens=[32768] * 32, hq=64, hkv=4, d=192,
                                 window=512 if config == 6 else 0, nan_tail=False,
-                                name=f"c{config}")
+                                kv_format="e4m3" if fp8 else "bf16", name=f"c{config}")
     raise SystemExit(f"unknown --config {config}")
 
 
@@ -303,6 +304,8 @@ def main():
     ap.add_argument("--prewarm", type=float, default=0.3,
                     help="seconds of untimed steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--fp8", action="store_true",
+                    help="configs 5 and 6 with an E4M3 cache (one fp32 scale per KV group)")
     ap.add_argument("--v-layout", choices=["channel", "subblock8"], default="channel",
                     help="V pool layout of the per-group configs (5, 6): channel-major, or "
                          "the 8-token sub-blocks the sparse global attention reads")
@@ -350,10 +353,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: building config {args.config} inputs")
-    case = make_case(args.config)
+    if args.fp8 and args.config not in (5, 6):
+        raise SystemExit("--fp8 selects the E4M3 cache of configs 5 and 6 (config 4 is E4M3 already)")
+    case = make_case(args.config, fp8=args.fp8)
     if hasattr(case, "host_slots"):   # drawn on the device
         t = {"q": case.q, "k": case.k, "v": case.v, "table": case.table, "lens": case.lens,
-             "k_scale": None, "v_scale": None,
+             "k_scale": case.k_scale, "v_scale": case.v_scale,
              "out": torch.empty((case.batch, case.hq, case.d), dtype=torch.bfloat16, device=dev)}
         cpu_case = case.host_slots([0, 1])
     else:

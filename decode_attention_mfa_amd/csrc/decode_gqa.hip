@@ -22,6 +22,8 @@
 // Each wave keeps its own online softmax (m, l, O) over its key subset; the
 // four are merged through LDS at the end (the same log-sum-exp merge as the
 // split combine).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernel_params.h"
 
@@ -39,26 +41,47 @@ __device__ __forceinline__ floatx4 mfma_bf16_16x16x16(intx2 a, intx2 b, floatx4 
                                                    __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
 }
 
-template <int D>
+// Tile geometry: bf16 or E4M3 (one byte per value) K/V.  The ring takes
+// 144 KB of LDS for d = 192 and 128 KB for d = 256, so E4M3 tiles keep twice
+// as many phases in flight.
+template <int D, bool kFp8>
 struct GqaCfg {
-  static constexpr int kPhaseBytes = 64 * D * 2;                  // one K or V^T tile
-  static constexpr int kRing = D == 192 ? 6 : 4;                   // LDS slots
+  static constexpr int kElem = kFp8 ? 1 : 2;                       // bytes per cached value
+  static constexpr int kPhaseBytes = 64 * D * kElem;               // one K or V^T tile
+  static constexpr int kRing = (D == 192 ? 147456 : 131072) / kPhaseBytes;   // LDS slots
   static constexpr int kAhead = kRing - 2;                         // phases in flight while computing
   static constexpr int kDmaPerWave = kPhaseBytes / 1024 / 4;       // 16-byte copies per lane per phase
-  static constexpr int kChunks = D / 8;                            // 16-byte chunks per K row
+  static constexpr int kChunks = D * kElem / 16;                   // 16-byte chunks per K row
+  static_assert(kRing % 2 == 0 && kAhead * kDmaPerWave < 64, "ring shape");
 };
 
-// K rows (2D bytes): XOR the chunk index with a key-dependent value so that
+// Eight E4M3 codes (two dwords) to the eight bf16 of an MFMA operand, and four
+// codes to four bf16: exact (every E4M3FN value is a bf16 value, scale 1).
+template <bool kUpper>
+__device__ __forceinline__ int e4m3x2_bf16x2(int w) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kUpper));
+}
+__device__ __forceinline__ intx4 e4m3x8_bf16(int w0, int w1) {
+  return intx4{e4m3x2_bf16x2<false>(w0), e4m3x2_bf16x2<true>(w0), e4m3x2_bf16x2<false>(w1),
+               e4m3x2_bf16x2<true>(w1)};
+}
+
+// K rows (D values): XOR the chunk index with a key-dependent value so that
 // the lanes of one MFMA operand read conflict-free (checked with the LDS
-// bank-conflict counter: folding key bit 3 into the d = 192 map cost every
-// K read a 2-way conflict).  d = 192 keeps the XOR inside aligned groups of
-// 8 chunks (24 chunks per row).
-template <int D>
+// bank-conflict counter: folding key bit 3 into the bf16 d = 192 map cost
+// every K read a 2-way conflict).  The XOR stays inside aligned groups of 8
+// chunks (bf16 d = 192: 24 chunks per row) or 4 (E4M3 d = 192: 12 chunks of
+// 16 codes, where key bits 1-2 are the conflict-free choice).
+template <int D, bool kFp8>
 __device__ __forceinline__ int swz_k(int key) {
+  if constexpr (kFp8) return D == 256 ? (key & 15) : ((key >> 1) & 3);
   return D == 256 ? (key & 15) : (key & 7);
 }
-// V^T rows (128 bytes, 8 chunks).
+// V^T rows: bf16 128 bytes (8 chunks of 8 keys), E4M3 64 bytes (4 chunks of
+// 16 keys; the 4-byte operand reads keep a 2-way bank conflict under every
+// XOR map of four chunks, and this one is among the best measured).
 __device__ __forceinline__ int swz_v(int ch) { return (ch & 7) ^ ((ch >> 3) & 1); }
+__device__ __forceinline__ int swz_v8(int ch) { return (ch >> 2) & 3; }
 
 template <int N>
 __device__ __forceinline__ void phase_barrier() {
@@ -68,9 +91,10 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
-__global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
-  using C = GqaCfg<D>;
+template <int D, bool kFp8>
+__global__ void __launch_bounds__(256) gqa_decode_kernel(DecodeParams p) {
+  using C = GqaCfg<D, kFp8>;
+  using T = std::conditional_t<kFp8, uint8_t, uint16_t>;     // cached value
   __shared__ __attribute__((aligned(1024))) uint8_t ring[C::kRing * C::kPhaseBytes];
   __shared__ int blk_ids[kMaxChunkTiles];
   __shared__ float wave_ml[4][kG][2];
@@ -117,24 +141,30 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
   for (int i = threadIdx.x; i < nt; i += 256)
     blk_ids[i] = p.block_table ? pool_block(p.block_table[(int64_t)b * p.max_blocks + t_begin + i], p.num_blocks) : 0;
 
-  // Q fragments: head r of the group, channels 32s + 8q4 .. +7.
+  // Q fragments: head r of the group.  bf16 K: step s takes channels
+  // 32s + 8q4 .. +7.  E4M3 K: step s takes channels 64(s/2) + 16q4 + 8(s%2)
+  // .. +7, so that one 16-byte read of codes holds the K operands of steps
+  // 2u and 2u + 1.
   intx4 qf[D / 32];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * D + q4 * 8;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * D;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[s] = *reinterpret_cast<const intx4*>(qp + s * 32);
+    for (int s = 0; s < D / 32; ++s)
+      qf[s] = *reinterpret_cast<const intx4*>(qp + (kFp8 ? 64 * (s >> 1) + 16 * q4 + 8 * (s & 1)
+                                                        : 32 * s + 8 * q4));
   }
   wait_vmcnt<0>();   // the copies below are invisible to the compiler's wait bookkeeping
   __syncthreads();
 
-  const uint16_t* kpool = static_cast<const uint16_t*>(p.k);
-  const uint16_t* vpool = static_cast<const uint16_t*>(p.v);
+  const T* kpool = static_cast<const T*>(p.k);
+  const T* vpool = static_cast<const T*>(p.v);
+  constexpr int kChunkElems = 16 / C::kElem;   // values per 16-byte chunk
   auto issue_phase = [&](int ph_req, uint8_t* dst) {
     const int ph = ph_req < nphase ? ph_req : nphase - 2 + (ph_req & 1);
     const int tile_rel = ph >> 1;
     const int tile = t_begin + tile_rel;
-    const uint16_t* kt;
-    const uint16_t* vt;
+    const T* kt;
+    const T* vt;
     if (p.block_table) {
       const int64_t blk = readfirstlane(blk_ids[tile_rel]);
       kt = kpool + blk * p.k_block_stride + (int64_t)g * p.k_head_stride;
@@ -144,25 +174,37 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
       vt = vpool + (int64_t)b * p.v_seq_stride + (int64_t)g * p.v_head_stride + (int64_t)tile * p.v_tile_stride;
     }
     if ((ph & 1) == 0) {
-      // K tile: 64 rows of D/8 chunks; copy i covers 1 KB = 64 chunks.
+      // K tile: 64 rows of kChunks chunks; copy i covers 1 KB = 64 chunks.
 #pragma unroll
       for (int k = 0; k < C::kDmaPerWave; ++k) {
         const int i = wave * C::kDmaPerWave + k;
         const int idx = i * 64 + lane;                 // chunk index in the tile
         const int row = idx / C::kChunks;
-        const int ch = (idx - row * C::kChunks) ^ swz_k<D>(row);
-        dma16(kt + row * p.k_row_stride + ch * 8, dst + i * 1024);
+        const int ch = (idx - row * C::kChunks) ^ swz_k<D, kFp8>(row);
+        dma16(kt + row * p.k_row_stride + ch * kChunkElems, dst + i * 1024);
       }
     } else {
       // V^T tile: D rows of 8 chunks (64 keys); copy i covers 8 rows.  Chunk
       // ch of row (channel) `row` is keys 8ch .. 8ch + 7 of that channel,
       // wherever the layout keeps them (channel-major or 8-token sub-blocks).
+      // E4M3: D rows of 4 chunks (16 keys each); copy i covers 16 rows, and
+      // V is channel-major (a chunk is 16 consecutive bytes).
+      if constexpr (kFp8) {
 #pragma unroll
-      for (int k = 0; k < C::kDmaPerWave; ++k) {
-        const int i = wave * C::kDmaPerWave + k;
-        const int row = 8 * i + (lane >> 3);
-        const int ch = (lane & 7) ^ swz_v(row);
-        dma16(vt + row * p.v_row_stride + ch * p.v_chunk_stride, dst + i * 1024);
+        for (int k = 0; k < C::kDmaPerWave; ++k) {
+          const int i = wave * C::kDmaPerWave + k;
+          const int row = 16 * i + (lane >> 2);
+          const int ch = (lane & 3) ^ swz_v8(row);
+          dma16(vt + row * p.v_row_stride + ch * 16, dst + i * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < C::kDmaPerWave; ++k) {
+          const int i = wave * C::kDmaPerWave + k;
+          const int row = 8 * i + (lane >> 3);
+          const int ch = (lane & 7) ^ swz_v(row);
+          dma16(vt + row * p.v_row_stride + ch * p.v_chunk_stride, dst + i * 1024);
+        }
       }
     }
   };
@@ -171,8 +213,8 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
   for (int ph = 0; ph < C::kRing - 1; ++ph) issue_phase(ph, ring + ph * C::kPhaseBytes);
 
   const int my_key = 16 * wave + r;                    // K operand row of this lane
-  const int xk = swz_k<D>(my_key);
-  const int xv = swz_v(r);
+  const int xk = swz_k<D, kFp8>(my_key);
+  const int xv = kFp8 ? swz_v8(r) : swz_v(r);
 
   float m_run = kNegInf;
   float l_run = 0.f;
@@ -183,11 +225,21 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
 
   auto k_phase = [&](const uint8_t* buf, int key0) {
     floatx4 st = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      const int chunk = (4 * s + q4) ^ xk;
-      const intx4 a = *reinterpret_cast<const intx4*>(buf + my_key * (2 * D) + chunk * 16);
-      st = mfma_bf16_16x16x32(a, qf[s], st);
+      for (int u = 0; u < D / 64; ++u) {
+        const int chunk = (4 * u + q4) ^ xk;
+        const intx4 c = *reinterpret_cast<const intx4*>(buf + my_key * D + chunk * 16);
+        st = mfma_bf16_16x16x32(e4m3x8_bf16(c.x, c.y), qf[2 * u], st);
+        st = mfma_bf16_16x16x32(e4m3x8_bf16(c.z, c.w), qf[2 * u + 1], st);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const int chunk = (4 * s + q4) ^ xk;
+        const intx4 a = *reinterpret_cast<const intx4*>(buf + my_key * (2 * D) + chunk * 16);
+        st = mfma_bf16_16x16x32(a, qf[s], st);
+      }
     }
     float sv[4];
     const bool partial = (key0 < lo) || (key0 + kPage > L);
@@ -230,11 +282,19 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
       keep0 = ((kfirst + 0 < vvalid) ? 0x0000ffffu : 0u) | ((kfirst + 1 < vvalid) ? 0xffff0000u : 0u);
       keep1 = ((kfirst + 2 < vvalid) ? 0x0000ffffu : 0u) | ((kfirst + 3 < vvalid) ? 0xffff0000u : 0u);
     }
-    const int chunk = (kfirst >> 3) ^ xv;
-    const int half = (q4 & 1) * 8;
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) {
-      intx2 a = *reinterpret_cast<const intx2*>(buf + ct * 2048 + r * 128 + chunk * 16 + half);
+      intx2 a;
+      if constexpr (kFp8) {
+        // Codes of keys kfirst .. +3: chunk kfirst / 16 of row 16 ct + r, byte
+        // kfirst % 16.
+        const uint32_t c = *reinterpret_cast<const uint32_t*>(
+            buf + ct * 1024 + r * 64 + (((kfirst >> 4) ^ xv) << 4) + (kfirst & 15));
+        a = intx2{e4m3x2_bf16x2<false>((int)c), e4m3x2_bf16x2<true>((int)c)};
+      } else {
+        a = *reinterpret_cast<const intx2*>(buf + ct * 2048 + r * 128 + (((kfirst >> 3) ^ xv) << 4) +
+                                            (q4 & 1) * 8);
+      }
       a.x &= keep0;
       a.y &= keep1;
       acc[ct] = mfma_bf16_16x16x16(a, pb, acc[ct]);
@@ -313,12 +373,16 @@ __global__ void __launch_bounds__(256) gqa_decode_bf16_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_gqa(const DecodeParams& p, int d, hipStream_t stream) {
+hipError_t launch_gqa(const DecodeParams& p, int d, bool fp8, hipStream_t stream) {
   dim3 grid(p.splits, p.batch * p.hkv);
-  if (d == 192)
-    hipLaunchKernelGGL(gqa_decode_bf16_kernel<192>, grid, dim3(256), 0, stream, p);
+  if (d == 192 && !fp8)
+    hipLaunchKernelGGL((gqa_decode_kernel<192, false>), grid, dim3(256), 0, stream, p);
+  else if (d == 256 && !fp8)
+    hipLaunchKernelGGL((gqa_decode_kernel<256, false>), grid, dim3(256), 0, stream, p);
+  else if (d == 192)
+    hipLaunchKernelGGL((gqa_decode_kernel<192, true>), grid, dim3(256), 0, stream, p);
   else if (d == 256)
-    hipLaunchKernelGGL(gqa_decode_bf16_kernel<256>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gqa_decode_kernel<256, true>), grid, dim3(256), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

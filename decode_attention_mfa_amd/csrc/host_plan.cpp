@@ -24,9 +24,11 @@ int path_for(int32_t group, int32_t d, int32_t kv) {
   return -1;
 }
 
-// FP8 storage: only the shared-tile MQA kernel reads E4M3 codes (it widens
-// them to bf16 MFMA operands itself).
-bool fp8_supported(int path) { return path == (int)DecodePath::kMqaShared; }
+// FP8 storage: the shared-tile MQA kernel and the per-group kernel read E4M3
+// codes (each widens them to bf16 MFMA operands itself); the fp32 path does not.
+bool fp8_supported(int path) {
+  return path == (int)DecodePath::kMqaShared || path == (int)DecodePath::kGqaSplitKeys;
+}
 
 }  // namespace
 

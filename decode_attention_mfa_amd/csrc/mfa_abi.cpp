@@ -11,7 +11,7 @@
 
 namespace mfa {
 hipError_t launch_mqa(const DecodeParams& p, bool fp8, hipStream_t stream);
-hipError_t launch_gqa(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_gqa(const DecodeParams& p, int d, bool fp8, hipStream_t stream);
 hipError_t launch_f32(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, int new_dtype, int kv_dtype, hipStream_t stream);
@@ -160,6 +160,7 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
   const mfa::DecodePlan pl = mfa::plan_decode(d, window, cus, tps);
   // Sub-blocked V is read by the per-group bf16 path only.
   if (v_layout == MFA_V_SUBBLOCK8 && pl.path != mfa::DecodePath::kGqaSplitKeys) return MFA_ERR_SHAPE;
+  if (v_layout == MFA_V_SUBBLOCK8 && d->kv_dtype != MFA_BF16) return MFA_ERR_DTYPE;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return MFA_ERR_WORKSPACE;
 
@@ -175,7 +176,7 @@ mfa_status decode_impl(const mfa_decode_desc* d0, int32_t tq, const void* q, con
       e = mfa::launch_mqa(p, d->kv_dtype == MFA_FP8_E4M3, s);
       break;
     case mfa::DecodePath::kGqaSplitKeys:
-      e = mfa::launch_gqa(p, d->head_dim, s);
+      e = mfa::launch_gqa(p, d->head_dim, d->kv_dtype == MFA_FP8_E4M3, s);
       break;
     case mfa::DecodePath::kF32:
       e = mfa::launch_f32(p, d->head_dim, s);

@@ -113,7 +113,8 @@ typedef enum mfa_dtype {
  *                       lengths only, and are bit-identical across runs.
  * Supported (Hq/Hkv, d): (64, 256) on the shared-tile MFMA path (MQA);
  * (16, 192), (16, 256) on the per-group MFMA path (GQA); any Hq/Hkv and any
- * d <= 256 that is a multiple of 4 with F32 storage.
+ * d <= 256 that is a multiple of 4 with F32 storage.  Both MFMA paths read
+ * BF16 or FP8_E4M3 caches (one fp32 scale per KV head).
  */
 typedef struct mfa_decode_desc {
   int32_t batch;
@@ -257,8 +258,8 @@ typedef enum mfa_v_layout {
  * eigentliche Attention liest weiterhin originale K/V").  The result is
  * bit-identical to the channel-major call on the same values.
  * MFA_V_SUBBLOCK8 is read by the per-group bf16 path only ((Hq/Hkv, d) =
- * (16, 192) or (16, 256), bf16 cache); other shapes return MFA_ERR_SHAPE.
- * Other v_layout values return MFA_ERR_ARG.
+ * (16, 192) or (16, 256)); other shapes return MFA_ERR_SHAPE and an E4M3
+ * cache MFA_ERR_DTYPE.  Other v_layout values return MFA_ERR_ARG.
  */
 mfa_status mfa_decode_attention_gqa_layout(const mfa_decode_desc* desc, const void* q,
                                            const void* k_cache, const void* v_cache,

@@ -93,10 +93,13 @@ def test_shape_rules():
     assert call_gqa(desc(num_q_heads=64, num_kv_heads=3), 0) == MFA_ERR_SHAPE  # 64 % 3
 
 
-def test_fp8_only_on_the_shared_tile_path():
-    # 16 heads per group (the key-split kernel) has no FP8 variant
+def test_fp8_on_the_mfma_paths_only():
+    # 16 heads per group reads E4M3 too: it then needs both scales ...
     assert call_gqa(desc(num_q_heads=64, num_kv_heads=4, head_dim=192,
-                         kv_dtype=MFA_FP8_E4M3), 0) == MFA_ERR_DTYPE
+                         kv_dtype=MFA_FP8_E4M3), 0) == MFA_ERR_NULL
+    # ... while a shape that only the fp32 kernel serves is refused for E4M3
+    assert call_gqa(desc(num_q_heads=64, num_kv_heads=4, head_dim=128,
+                         kv_dtype=MFA_FP8_E4M3), 0) == MFA_ERR_SHAPE
 
 
 def test_alignment_scale_window_workspace():
@@ -272,6 +275,10 @@ def test_v_layout_and_incremental_summary_rules():
     assert gqa_layout(desc(num_splits=1), 1) == MFA_ERR_SHAPE                  # MQA shape
     assert gqa_layout(desc(q_dtype=MFA_F32, kv_dtype=MFA_F32, out_dtype=MFA_F32,
                            **step5), 1) == MFA_ERR_SHAPE                       # fp32 path
+    lib_fp8 = lib.mfa_decode_attention_gqa_layout(
+        ctypes.byref(desc(kv_dtype=MFA_FP8_E4M3, **step5)), A, A, A, A, A, A, A, A,
+        ctypes.c_float(0.07), ctypes.c_int32(0), ctypes.c_int32(1), None, ctypes.c_size_t(0), None)
+    assert lib_fp8 == MFA_ERR_DTYPE                                            # E4M3 stays channel-major
 
     def append(kv_dtype, new_dtype, layout):
         d = MfaKvAppendDesc(batch=4, num_kv_heads=4, head_dim=192, page_size=64,
