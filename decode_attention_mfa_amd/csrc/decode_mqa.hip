@@ -601,9 +601,22 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
     // Split partials are read once, by the merge kernel: streamed out rather
     // than kept dirty in L2 for the write-back at the kernel's end.
     const int64_t row = piece * kRows + (head - g * kRows);
+    if (p.part_bf16) {
+      // bf16 rows: tiles 2j and 2j+1 of this lane form run 4j + q4 (8
+      // elements), so the four q4 lanes of a head write 64 contiguous bytes.
+      uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + row * kD + q4 * 8;
 #pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct)
-      __builtin_nontemporal_store(acc[ct], reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4));
+      for (int j = 0; j < kD / 32; ++j)
+        __builtin_nontemporal_store(
+            intx4{(int)pack_bf16x2(acc[2 * j].x, acc[2 * j].y), (int)pack_bf16x2(acc[2 * j].z, acc[2 * j].w),
+                  (int)pack_bf16x2(acc[2 * j + 1].x, acc[2 * j + 1].y),
+                  (int)pack_bf16x2(acc[2 * j + 1].z, acc[2 * j + 1].w)},
+            reinterpret_cast<intx4*>(po + j * 32));
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct)
+        __builtin_nontemporal_store(acc[ct], reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4));
+    }
     if (q4 == 0) __builtin_nontemporal_store(floatx2{m_run, l_tot}, reinterpret_cast<floatx2*>(p.part_ml + row * 2));
   };
 

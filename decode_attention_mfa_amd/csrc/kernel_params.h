@@ -33,6 +33,7 @@ struct DecodeParams {
   const float* v_scale;
   void* out;                  // [B, Hq, d]
   float* part_o;              // [B*Hkv, splits, G, d]   (splits > 1)
+  int32_t part_bf16;          // 1: part_o holds bf16 values (uint16_t), else fp32
   float* part_ml;             // [B*Hkv, splits, G, 2]   (splits > 1)
   // Balanced partition (MQA, paged, dense): the batch's pages are cut into
   // equal ranges, one per workgroup of a 1-D grid of G; partials then live

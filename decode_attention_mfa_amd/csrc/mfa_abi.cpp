@@ -76,6 +76,9 @@ mfa::DecodeParams make_params(const mfa_decode_desc* d, const mfa::DecodePlan& p
   p.splits = pl.splits;
   p.chunk_tiles = pl.chunk_pages;
   p.out_f32 = d->out_dtype == MFA_F32;
+  // A bf16 result needs no more than bf16 partials from the shared-tile
+  // kernel (half the partial traffic); an fp32 result keeps fp32 partials.
+  p.part_bf16 = pl.path == mfa::DecodePath::kMqaShared && !p.out_f32;
   const int64_t hd = d->head_dim, hkv = d->num_kv_heads;
   if (block_table) {
     p.k_block_stride = hkv * kPage * hd;
