@@ -86,11 +86,14 @@ __device__ __forceinline__ void keep(floatx8 v) {
   asm volatile("" ::"v"(floatx4{v[0], v[1], v[2], v[3]}), "v"(floatx4{v[4], v[5], v[6], v[7]}));
 }
 
-// Merge row of this thread: 4 waves per workgroup, kRowsPerWave rows per wave.
-template <bool kBf16>
+// Merge row of this thread: 4 waves per workgroup, kRowsPerWave rows per wave;
+// workgroups numbered XCD-major when kXcd (the balanced merge: a slot's rows
+// then run on the XCD whose attention workgroups wrote its pieces).
+template <bool kBf16, bool kXcd = false>
 __device__ __forceinline__ int64_t merge_row() {
   constexpr int kR = MergeLane<kBf16>::kRowsPerWave;
-  return ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kR + (kR == 2 ? (threadIdx.x & 63) >> 5 : 0);
+  const int64_t wg = kXcd ? xcd_major(blockIdx.x, gridDim.x) : blockIdx.x;
+  return (wg * 4 + (threadIdx.x >> 6)) * kR + (kR == 2 ? (threadIdx.x & 63) >> 5 : 0);
 }
 
 template <int kMaxSplits, bool kBf16>
@@ -183,7 +186,7 @@ __global__ void __launch_bounds__(256) combine_balanced_kernel(DecodeParams p) {
   using Lane = MergeLane<kBf16>;
   using vec = typename Lane::vec;
   const Lane ln(threadIdx.x & 63, kD);
-  const int64_t row = merge_row<kBf16>();   // over B*Hq
+  const int64_t row = merge_row<kBf16, true>();   // over B*Hq
   if (row >= (int64_t)p.batch * p.hq) return;
   const int b = (int)(row / p.hq);
   const int h = (int)(row - (int64_t)b * p.hq);

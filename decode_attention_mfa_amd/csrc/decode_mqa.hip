@@ -221,6 +221,11 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   int b = bg / p.hkv;          // slot (changes per piece under the balanced partition)
   const int g = bg - b * p.hkv;
   const int split = kBal ? 0 : blockIdx.x;
+  // Balanced partition: the workgroup's place in the cut, numbered XCD-major
+  // (launch slots go round-robin over the 8 XCDs), so that consecutive
+  // ranges -- the pieces of one slot -- run on one XCD, where the merge
+  // kernel reads them back.
+  const int wl = kBal ? xcd_major(blockIdx.x, gridDim.x) : 0;
   const int32_t* trow = p.block_table ? p.block_table + (int64_t)seq_of(p, b) * p.max_blocks : nullptr;
 
   // Dense attention: the split's first page (split * chunk) does not depend
@@ -234,8 +239,8 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   // (workgroup w = slot w / splits, pages from (w % splits) * chunk), so
   // those block ids are fetched alongside the lengths and used if the real
   // partition agrees.
-  const int spec_b = kBal ? (int)blockIdx.x / p.splits : 0;
-  const int spec_pg = kBal ? ((int)blockIdx.x - spec_b * p.splits) * p.chunk_tiles : 0;
+  const int spec_b = kBal ? wl / p.splits : 0;
+  const int spec_pg = kBal ? (wl - spec_b * p.splits) * p.chunk_tiles : 0;
   const int32_t* spec_row = kBal ? p.block_table + (int64_t)seq_of(p, spec_b) * p.max_blocks : trow;
   int blk_first[kFirstTiles];
 #pragma unroll
@@ -401,9 +406,9 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
     const int ge_spec = max(1, min((int)gridDim.x, tot_spec / kMinBalancedPages));
     int pred_b = 0, pred_pg = 0;
     bool spec_issued = false;
-    if (l_first == l_spec && l_last == l_spec && p_spec > 0 && (int)blockIdx.x < ge_spec) {
-      const int s_pred = (int)((int64_t)blockIdx.x * tot_spec / ge_spec);
-      const int e_pred = (int)((int64_t)(blockIdx.x + 1) * tot_spec / ge_spec);
+    if (l_first == l_spec && l_last == l_spec && p_spec > 0 && wl < ge_spec) {
+      const int s_pred = (int)((int64_t)wl * tot_spec / ge_spec);
+      const int e_pred = (int)((int64_t)(wl + 1) * tot_spec / ge_spec);
       pred_b = s_pred / p_spec;
       pred_pg = s_pred - pred_b * p_spec;
       spec_issued = e_pred - s_pred >= kFirstTiles && pred_pg + kFirstTiles <= p_spec;
@@ -475,7 +480,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
         bal_len[kSpt * tid + k] = len[k];
       }
       const int ge = max(1, min((int)gridDim.x, total / kMinBalancedPages));
-      const int w = blockIdx.x;
+      const int w = wl;
       const bool active = total > 0 && w < ge;
       const int s_w = active ? (int)((int64_t)w * total / ge) : 0;
       const int e_w = active ? (int)((int64_t)(w + 1) * total / ge) : 0;
@@ -885,7 +890,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
         Lq = query_keys(L);
         pg_first = page;
       } else if (slot != b) {
-        store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + blockIdx.x);
+        store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + wl);
         ++piece;
         b = slot;
         load_q();
@@ -903,7 +908,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       lds_barrier();   // V^T tile visible
       v_phase();
     }
-    store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + blockIdx.x);
+    store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + wl);
     return;
   }
   for (int t = 0; t < nt; ++t) {

@@ -116,4 +116,12 @@ __device__ __forceinline__ float wave_sum_xor16_32(float x) {
 
 __device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// XCD-major number of launch slot x of a 1-D grid of n workgroups: slots go
+// round-robin over the 8 XCDs, so slot x runs on XCD x % 8 and gets number
+// (x % 8) * (n / 8) + x / 8; numbers k * n/8 .. (k+1) * n/8 - 1 share XCD k.
+// (Identity when n is not a multiple of 8.)
+__device__ __forceinline__ int xcd_major(int x, int n) {
+  return (n & 7) ? x : (x & 7) * (n >> 3) + (x >> 3);
+}
+
 }  // namespace mfa
