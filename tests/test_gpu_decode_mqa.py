@@ -48,6 +48,35 @@ def test_mqa_bf16_paged_ragged(splits):
     assert torch.all(got[6] == 0)          # empty slot
 
 
+@pytest.mark.parametrize("out_format", ["bf16", "f32"])
+def test_more_than_eight_splits(out_format):
+    # Twelve forced splits take the running merge over any split count, with
+    # bf16 partials (bf16 result) or fp32 ones (fp32 result).
+    case = make_decode_case(111, batch=len(RAGGED), ctx_lens=RAGGED, hq=64, hkv=1, d=256,
+                            scale=1 / 16)
+    t = to_device(case, out_format=out_format)
+    got = run_decode(case, t, num_splits=12).clone()
+    assert_parity(got, oracle(case), "bf16", f"12 splits, {out_format} out")
+    again = run_decode(case, t, num_splits=12)
+    assert torch.equal(got, again)
+
+
+@pytest.mark.parametrize("batch", [7, 8, 13])
+@pytest.mark.parametrize("out_format", ["bf16", "f32"])
+def test_balanced_partition_grid_sizes(batch, out_format):
+    # The balanced cut numbers its workgroups XCD-major when the grid is a
+    # multiple of 8 and in launch order otherwise; the merge finds the pieces
+    # either way, with bf16 or fp32 partials.
+    rng = np.random.default_rng(1000 + batch)
+    lens = rng.integers(700, 3000, size=batch).tolist()
+    case = make_decode_case(112 + batch, batch=batch, ctx_lens=lens, hq=64, hkv=1, d=256,
+                            scale=1 / 16)
+    t = to_device(case, out_format=out_format)
+    got = run_decode(case, t, num_splits=0)
+    assert_parity(got, oracle(case), "bf16", f"balanced, batch {batch}, {out_format} out",
+                  per_slot=True)
+
+
 def test_mqa_bf16_contiguous_cache():
     case = make_decode_case(102, batch=3, ctx_lens=[200, 64, 1], hq=64, hkv=1, d=256,
                             paged=False, scale=1 / 16)
