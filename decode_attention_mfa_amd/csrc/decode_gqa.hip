@@ -12,9 +12,9 @@
 // Workgroup = 4 waves = one (slot, KV group, split).  The split's keys are
 // streamed in 64-key tiles through the same LDS phase ring as the MQA kernel
 // (phase 2t = K tile [64][d], phase 2t+1 = V^T tile [d][64], 16-byte
-// global->LDS DMA, kRing - 2 phases in flight).  With 16 heads per group a
-// single MFMA row block covers all heads, so the waves split the keys
-// instead: wave w takes keys 16w .. 16w+15 of every tile.
+// non-temporal global->LDS DMA, kRing - 2 phases in flight).  With 16 heads
+// per group a single MFMA row block covers all heads, so the waves split the
+// keys instead: wave w takes keys 16w .. 16w+15 of every tile.
 //   S^T[key, head] = K . Q^T            16x16x32 bf16 MFMA, d/32 K-steps
 //   O^T[ch, head] += V^T . P^T          16x16x16 bf16 MFMA over the wave's
 //                                       16 keys (the S^T lane layout is the
@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(256) gqa_decode_kernel(DecodeParams p) {
         const int idx = i * 64 + lane;                 // chunk index in the tile
         const int row = idx / C::kChunks;
         const int ch = (idx - row * C::kChunks) ^ swz_k<D, kFp8>(row);
-        dma16(kt + row * p.k_row_stride + ch * kChunkElems, dst + i * 1024);
+        dma16_nt(kt + row * p.k_row_stride + ch * kChunkElems, dst + i * 1024);
       }
     } else {
       // V^T tile: D rows of 8 chunks (64 keys); copy i covers 8 rows.  Chunk
@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(256) gqa_decode_kernel(DecodeParams p) {
           const int i = wave * C::kDmaPerWave + k;
           const int row = 16 * i + (lane >> 2);
           const int ch = (lane & 3) ^ swz_v8(row);
-          dma16(vt + row * p.v_row_stride + ch * 16, dst + i * 1024);
+          dma16_nt(vt + row * p.v_row_stride + ch * 16, dst + i * 1024);
         }
       } else {
 #pragma unroll
@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(256) gqa_decode_kernel(DecodeParams p) {
           const int i = wave * C::kDmaPerWave + k;
           const int row = 8 * i + (lane >> 3);
           const int ch = (lane & 7) ^ swz_v(row);
-          dma16(vt + row * p.v_row_stride + ch * p.v_chunk_stride, dst + i * 1024);
+          dma16_nt(vt + row * p.v_row_stride + ch * p.v_chunk_stride, dst + i * 1024);
         }
       }
     }

