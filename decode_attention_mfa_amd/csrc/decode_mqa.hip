@@ -56,7 +56,7 @@ namespace {
 
 constexpr int kD = 256;
 constexpr int kG = 64;
-constexpr int kLoaders = 256;          // four loader waves (plus 4 or 8 compute waves)
+constexpr int kLoaders = 256;          // four loader waves (plus four compute waves)
 constexpr int kPhaseBytes = 32768;     // one bf16 K or V^T tile in LDS
 constexpr int kMaxChunkTiles = 2048;   // block ids cached per workgroup
 constexpr int kMaxBalancedSlots = 512; // balanced partition: slots per batch at most
@@ -171,16 +171,18 @@ __device__ __forceinline__ void unroll(F&& f) {
 //
 // kTps = 2 (multi-token queries, an even number per sequence): a query slot
 // is a pair of consecutive new tokens, 128 query rows over one cache row, so
-// each K/V tile is read once for both.  Eight compute waves (wave w: token
-// w/4 of the pair, heads 16(w%4) ..) and the four loaders, 12 waves; the
-// first token of the pair attends one key fewer than the second.
+// each K/V tile is read once for both.  Compute wave w holds heads 16w ..
+// 16w + 15 of both tokens: softmax state, accumulators and P operands are
+// per token, and every K or V^T operand read from LDS (and, FP8, widened)
+// feeds one product per token.  The first token of the pair attends one key
+// fewer than the second.
 template <bool kDense, bool kFp8, bool kK8, bool kV8, bool kBal, int kTps>
-__global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams p) {
   static_assert(kFp8 || (!kK8 && !kV8), "8-bit LDS tiles need an FP8 cache");
   static_assert(kK8 || !kV8, "8-bit V^T tiles use the 8-bit K key map");
   static_assert(!kBal || kDense, "the balanced partition covers dense attention");
   static_assert(kTps == 1 || (kTps == 2 && kDense), "token pairs are built for dense attention");
-  constexpr int kCw = 4 * kTps;                       // compute waves
+  constexpr int kCw = 4;                              // compute waves (each holds every token of a slot)
   constexpr int kCt = 64 * kCw;                       // compute threads
   constexpr int kNt = kCt + kLoaders;                 // threads
   constexpr int kRows = kG * kTps;                    // query rows per slot and KV group
@@ -194,14 +196,13 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   constexpr int kKSlot = kK8 ? kPhaseBytes / 2 : kPhaseBytes;   // LDS bytes of a K tile
   constexpr int kVSlot = kV8 ? kPhaseBytes / 2 : kPhaseBytes;   // and of a V^T tile
   // Phases in flight in the loaders' registers: 4 bf16 or 8 FP8 phases,
-  // 128 KB of cache data per CU either way (6 FP8 phases for token pairs,
-  // whose twelve waves have 168 registers per lane).
-  constexpr int kStages = kFp8 ? (kTps == 2 ? 6 : 8) : 4;
+  // 128 KB of cache data per CU either way.
+  constexpr int kStages = kFp8 ? 8 : 4;
   constexpr int kFirstTiles = (kStages + 1) / 2;      // tiles the start-up loads touch
   __shared__ __attribute__((aligned(1024))) uint8_t kslot[kKSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t vslot[kVSlot];
   __shared__ int blk_ids[kMaxChunkTiles];
-  __shared__ intx4 qlds[kTps == 2 ? kCw * (kD / 32) * 64 : 1];   // token pairs: Q fragments
+  __shared__ intx4 qlds[kTps == 2 ? kCw * kTps * (kD / 32) * 64 : 1];   // token pairs: Q fragments
   // Balanced partition: first global page and length of every slot, each
   // tile's (slot << 20 | page) and keys below the slot end, scan partials, a
   // counter the compute waves synchronise on, and {tiles, speculation held}.
@@ -360,33 +361,50 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
 
   // ---- compute-wave identity ----
   const int hg = wave & 3;     // head group: heads 16hg .. 16hg+15 of the KV group
-  const int tk = kTps == 1 ? 0 : (wave >> 2);   // token of a pair
   const int r = lane & 15;     // MFMA row / column of this lane
   const int q4 = lane >> 4;    // K-group of this lane
-  const int head = g * kRows + tk * kG + hg * 16 + r;    // this lane's query row
+  // This lane's query row for token tk of the slot (one token, or a pair).
+  const int head = g * kRows + hg * 16 + r;
+  auto head_of = [&](int tk) __attribute__((always_inline)) { return head + tk * kG; };
+  // Token pairs: the per-piece code (query loads, result stores) inside the
+  // balanced partition's tile loop forms its lane addresses afresh from a
+  // copy of the lane index that the compiler cannot see through, rather
+  // than hoisting them out of the loop into registers the accumulators of
+  // two tokens need.
+  struct LaneIds {
+    int ln, q4, head;   // lane, K-group, token-0 query row
+  };
+  auto lane_ids = [&]() __attribute__((always_inline)) {
+    int ln = lane;
+    if constexpr (kTps == 2) asm volatile("" : "+v"(ln));
+    return LaneIds{ln, ln >> 4, g * kRows + hg * 16 + (ln & 15)};
+  };
   // Q fragments (B operand of S^T): this lane's head, channels 32c + 8q4 ..
-  // +7 (FP8: 64(c/2) + 16q4 + 8(c%2) .. +7).
-  // With token pairs (twelve waves, 168 registers per lane) each compute
-  // wave parks its fragments in its own LDS rows and reads them back per K
-  // tile, so that they are not held across the V phase.
+  // +7 (FP8: 64(c/2) + 16q4 + 8(c%2) .. +7).  With token pairs each compute
+  // wave parks both tokens' fragments in its own LDS rows and reads them
+  // back per K tile, so that they are not held across the V phase.
   intx4 qf[kD / 32];
-  auto load_q = [&]() __attribute__((always_inline)) {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + head) * kD;
+  auto load_q = [&](int slot) __attribute__((always_inline)) {
+    const LaneIds id = lane_ids();
 #pragma unroll
-    for (int c = 0; c < kD / 32; ++c) {
-      const int ch = kMap16 ? 64 * (c >> 1) + 16 * q4 + 8 * (c & 1) : 32 * c + 8 * q4;
-      qf[c] = *reinterpret_cast<const intx4*>(qp + ch);
-    }
-    if constexpr (kTps == 2) {
+    for (int tk = 0; tk < kTps; ++tk) {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)slot * p.hq + id.head + tk * kG) * kD;
 #pragma unroll
-      for (int c = 0; c < kD / 32; ++c) qlds[(wave * (kD / 32) + c) * 64 + lane] = qf[c];
+      for (int c = 0; c < kD / 32; ++c) {
+        const int ch = kMap16 ? 64 * (c >> 1) + 16 * id.q4 + 8 * (c & 1) : 32 * c + 8 * id.q4;
+        qf[c] = *reinterpret_cast<const intx4*>(qp + ch);
+      }
+      if constexpr (kTps == 2) {
+#pragma unroll
+        for (int c = 0; c < kD / 32; ++c) qlds[((wave * kTps + tk) * (kD / 32) + c) * 64 + id.ln] = qf[c];
+      }
     }
   };
-  auto qfrag = [&](int c) __attribute__((always_inline)) {
+  auto qfrag = [&](int tk, int c) __attribute__((always_inline)) {
     if constexpr (kTps == 1)
       return qf[c];
     else
-      return qlds[(wave * (kD / 32) + c) * 64 + lane];
+      return qlds[((wave * kTps + tk) * (kD / 32) + c) * 64 + lane];
   };
 
   // ---- balanced partition: this workgroup's slot pieces and tile list ----
@@ -426,7 +444,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       }
     } else {
       b = spec_b;
-      load_q();
+      load_q(b);
       // Block ids of the split plan's pages for this workgroup, fetched
       // with the lengths (tile i = tid + kCt k); used where the partition
       // agrees.
@@ -530,7 +548,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       }
       if (b0 != b) {
         b = b0;
-        load_q();
+        load_q(b);
       }
     }
     lds_barrier();   // tile list, block ids, key counts and phase 0 visible
@@ -547,10 +565,14 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   }
 
   const int lo = (!kDense && L > p.window) ? L - p.window : 0;
-  // Keys this compute wave's token attends: the slot's (its last token's)
-  // length, one fewer for the first token of a pair.
-  auto query_keys = [&](int len) __attribute__((always_inline)) { return kTps == 1 ? len : max(len - (kTps - 1 - tk), 0); };
-  int Lq = query_keys(L);
+  // Keys token tk of the slot attends: the slot's (its last token's) length,
+  // one fewer for the first token of a pair.
+  int Lq[kTps];
+  auto set_query_keys = [&](int len) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tk = 0; tk < kTps; ++tk) Lq[tk] = max(len - (kTps - 1 - tk), 0);
+  };
+  set_query_keys(L);
   int n_tiles = 0, t_lo = 0;
   if (L > 0) {
     t_lo = lo / kPage;
@@ -564,68 +586,85 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   const bool empty = !kBal && (t_begin >= t_end || (kDense && split * p.chunk_tiles >= p.max_blocks));
   if (empty && p.splits == 1) {
     if (loader) return;
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
-      if (p.out_f32)
-        *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
-      else
-        *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
-    }
+    for (int tk = 0; tk < kTps; ++tk)
+      for (int ct = 0; ct < kD / 16; ++ct) {
+        const int64_t o = ((int64_t)b * p.hq + head_of(tk)) * kD + ct * 16 + q4 * 4;
+        if (p.out_f32)
+          *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = floatx4{0.f, 0.f, 0.f, 0.f};
+        else
+          *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) = intx2{0, 0};
+      }
     return;
   }
   const int nt = kBal ? bal_nt : (empty ? 0 : t_end - t_begin);
   nphase = 2 * nt;
 
-  // Online-softmax state of a compute lane (head `head`, channels
-  // 16ct + 4q4 .. +3 of O^T tile ct).
-  float m_run = kNegInf;
-  float l_run = 0.f;
-  floatx4 acc[kD / 16];
+  // Online-softmax state of a compute lane, per token tk (row head_of(tk),
+  // channels 16ct + 4q4 .. +3 of O^T tile ct).
+  float m_run[kTps], l_run[kTps];
+  floatx4 acc[kTps][kD / 16];
+  auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tk = 0; tk < kTps; ++tk) {
+      m_run[tk] = kNegInf;
+      l_run[tk] = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < kD / 16; ++ct) acc[tk][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  reset_state();
 
   // A compute wave holds every key of its 16 heads for the piece it has
   // walked: the final output of slot b, or partial `piece` for the merge.
   auto store_result = [&](bool final_out, int64_t piece) __attribute__((always_inline)) {
-    const float l_tot = wave_sum_xor16_32(l_run);
-    if (final_out) {
-      // (The first token of a pair may have no key at all: zeros.)
-      const float inv = (kTps == 1 || l_tot > 0.f) ? (kFp8 ? p.v_scale[g] : 1.f) / l_tot : 0.f;
+    const LaneIds id = lane_ids();
 #pragma unroll
-      for (int ct = 0; ct < kD / 16; ++ct) {
-        const int64_t o = ((int64_t)b * p.hq + head) * kD + ct * 16 + q4 * 4;
-        const floatx4 v = acc[ct] * inv;
-        if (p.out_f32)
-          *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = v;
-        else
-          *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) =
-              intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
+    for (int tk = 0; tk < kTps; ++tk) {
+      const float l_tot = wave_sum_xor16_32(l_run[tk]);
+      if (final_out) {
+        // (The first token of a pair may have no key at all: zeros.)
+        const float inv = (kTps == 1 || l_tot > 0.f) ? (kFp8 ? p.v_scale[g] : 1.f) / l_tot : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < kD / 16; ++ct) {
+          const int64_t o = ((int64_t)b * p.hq + (id.head + tk * kG)) * kD + ct * 16 + id.q4 * 4;
+          const floatx4 v = acc[tk][ct] * inv;
+          if (p.out_f32)
+            *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + o) = v;
+          else
+            *reinterpret_cast<intx2*>(static_cast<uint16_t*>(p.out) + o) =
+                intx2{(int)pack_bf16x2(v.x, v.y), (int)pack_bf16x2(v.z, v.w)};
+        }
+        continue;
       }
-      return;
-    }
-    // Split partials are read once, by the merge kernel.
-    const int64_t row = piece * kRows + (head - g * kRows);
-    if (p.part_bf16) {
-      // bf16 rows: tiles 2j and 2j+1 of this lane form run 4j + q4 (8
-      // elements), so the four q4 lanes of a head write 64 contiguous bytes.
-      // Plain stores: L2 joins the two 64-byte halves of each line (streamed
-      // out, the halves left separately: 12.2 MB written for 8.4 MB).
-      uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + row * kD + q4 * 8;
+      // Split partials are read once, by the merge kernel.
+      const int64_t row = piece * kRows + ((id.head + tk * kG) - g * kRows);
+      if (p.part_bf16) {
+        // bf16 rows: tiles 2j and 2j+1 of this lane form run 4j + q4 (8
+        // elements), so the four q4 lanes of a head write 64 contiguous
+        // bytes.  Plain stores: L2 joins the two 64-byte halves of each line
+        // (streamed out, the halves left separately: 12.2 MB written for
+        // 8.4 MB).
+        uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + row * kD + id.q4 * 8;
 #pragma unroll
-      for (int j = 0; j < kD / 32; ++j)
-        *reinterpret_cast<intx4*>(po + j * 32) =
-            intx4{(int)pack_bf16x2(acc[2 * j].x, acc[2 * j].y), (int)pack_bf16x2(acc[2 * j].z, acc[2 * j].w),
-                  (int)pack_bf16x2(acc[2 * j + 1].x, acc[2 * j + 1].y),
-                  (int)pack_bf16x2(acc[2 * j + 1].z, acc[2 * j + 1].w)};
-    } else {
-      // fp32 rows (whole 64-byte quarters of a line per store): streamed out
-      // rather than kept dirty in L2 for the write-back at the kernel's end.
+        for (int j = 0; j < kD / 32; ++j)
+          *reinterpret_cast<intx4*>(po + j * 32) =
+              intx4{(int)pack_bf16x2(acc[tk][2 * j].x, acc[tk][2 * j].y),
+                    (int)pack_bf16x2(acc[tk][2 * j].z, acc[tk][2 * j].w),
+                    (int)pack_bf16x2(acc[tk][2 * j + 1].x, acc[tk][2 * j + 1].y),
+                    (int)pack_bf16x2(acc[tk][2 * j + 1].z, acc[tk][2 * j + 1].w)};
+      } else {
+        // fp32 rows (whole 64-byte quarters of a line per store): streamed
+        // out rather than kept dirty in L2 for the write-back at the
+        // kernel's end.
 #pragma unroll
-      for (int ct = 0; ct < kD / 16; ++ct)
-        __builtin_nontemporal_store(acc[ct], reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + q4 * 4));
+        for (int ct = 0; ct < kD / 16; ++ct)
+          __builtin_nontemporal_store(acc[tk][ct], reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + id.q4 * 4));
+      }
+      if (id.q4 == 0)
+        __builtin_nontemporal_store(floatx2{m_run[tk], l_tot}, reinterpret_cast<floatx2*>(p.part_ml + row * 2));
     }
-    if (q4 == 0) __builtin_nontemporal_store(floatx2{m_run, l_tot}, reinterpret_cast<floatx2*>(p.part_ml + row * 2));
   };
+
 
   if (!empty) {
 
@@ -695,7 +734,7 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
   // ---------------- compute waves ----------------
   const float qk_scale = p.scale * kLog2e * (kFp8 ? p.k_scale[g] : 1.f);
   if constexpr (!kBal) {
-    load_q();
+    load_q(b);
     lds_barrier();   // block ids and phase 0 visible
   }
 
@@ -716,32 +755,60 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
                               : r * 128 + (((kMap16 ? 2 * q4 : q4) ^ swz_v<kMap16>(r)) << 4);
   const uint32_t vfrag1 = r * 128 + (((kMap16 ? 2 * q4 + 1 : 4 + q4) ^ swz_v<kMap16>(r)) << 4);
 
-  intx4 pb[2];
+  intx4 pb[kTps][2];
   // LDS operand reads issued ahead of the products (16-byte reads; FP8 K
-  // reads feed two products each).  Twelve-wave workgroups leave the order
-  // to the compiler's register-pressure-aware scheduler.
+  // reads feed two products each, per token).
   constexpr int kAhead = 8;
   constexpr int kAhead8 = 6;
 
   auto k_phase = [&](int key0) __attribute__((always_inline)) {
     uint32_t kb = kfrag;
     asm volatile("" : "+v"(kb));   // addresses formed here, not hoisted and kept live
-    floatx4 st[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 st[kTps][4];
+#pragma unroll
+    for (int tk = 0; tk < kTps; ++tk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st[tk][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     if constexpr (kK8) {
       intx4 raw[kD / 64][4];
+      intx4 qv[kD / 64][kTps][2];   // token pairs: Q fragments read back per K tile
 #pragma unroll
-      for (int u = 0; u < kD / 64; ++u)
+      for (int u = 0; u < kD / 64; ++u) {
+        if constexpr (kTps == 2) {
+#pragma unroll
+          for (int tk = 0; tk < kTps; ++tk) {
+            qv[u][tk][0] = qfrag(tk, 2 * u);
+            qv[u][tk][1] = qfrag(tk, 2 * u + 1);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           raw[u][j] = *reinterpret_cast<const intx4*>(kslot + (kb ^ (u << 6)) + j * 1024);
+      }
 #pragma unroll
       for (int u = 0; u < kD / 64; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].x, raw[u][j].y), qfrag(2 * u), st[j]);
-          st[j] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[u][j].z, raw[u][j].w), qfrag(2 * u + 1), st[j]);
+          // Each K operand is widened once and feeds every token's product.
+          const intx4 k_lo = e4m3x8_to_bf16(raw[u][j].x, raw[u][j].y);
+          const intx4 k_hi = e4m3x8_to_bf16(raw[u][j].z, raw[u][j].w);
+#pragma unroll
+          for (int tk = 0; tk < kTps; ++tk) {
+            st[tk][j] = mfma_bf16_16x16x32(k_lo, kTps == 1 ? qfrag(0, 2 * u) : qv[u][tk][0], st[tk][j]);
+            st[tk][j] = mfma_bf16_16x16x32(k_hi, kTps == 1 ? qfrag(0, 2 * u + 1) : qv[u][tk][1], st[tk][j]);
+          }
         }
-      if constexpr (kTps == 1) {
+      if constexpr (kTps == 2) {
+        // Per step u: four Q and four K reads feed sixteen products; one
+        // step of reads runs ahead.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 1; u < kD / 64; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      } else {
         __builtin_amdgcn_sched_group_barrier(0x100, kAhead8, 0);
 #pragma unroll
         for (int i = 0; i < 16 - kAhead8; ++i) {
@@ -752,8 +819,13 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       }
     } else {
       intx4 a[kD / 32][4];
+      intx4 qv[kD / 32][kTps];   // token pairs: Q fragments read back per K tile
 #pragma unroll
       for (int c = 0; c < kD / 32; ++c) {
+        if constexpr (kTps == 2) {
+#pragma unroll
+          for (int tk = 0; tk < kTps; ++tk) qv[c][tk] = qfrag(tk, c);
+        }
         const uint32_t a_off = kb ^ (c << 6);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -762,11 +834,23 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
 #pragma unroll
       for (int c = 0; c < kD / 32; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st[j] = mfma_bf16_16x16x32(a[c][j], qfrag(c), st[j]);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int tk = 0; tk < kTps; ++tk)
+            st[tk][j] = mfma_bf16_16x16x32(a[c][j], kTps == 1 ? qfrag(0, c) : qv[c][tk], st[tk][j]);
       // Software pipeline: operands of kAhead products in flight ahead of
-      // the matrix unit (the other wave on this SIMD is a loader; with token
-      // pairs, also the other token's compute wave).
-      if constexpr (kTps == 1) {
+      // the matrix unit (the other wave on this SIMD is a loader).  Token
+      // pairs: per chunk c, two Q and four K reads feed eight products; two
+      // chunks of reads run ahead.
+      if constexpr (kTps == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int c = 1; c < kD / 32; ++c) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      } else {
         __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
         for (int i = 0; i < 32 - kAhead; ++i) {
@@ -777,61 +861,64 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       }
     }
     // Lane values: tile j, element i is key key0 + 8q4 + 32(j/2) + 4(j%2) + i
-    // (FP8: key0 + 16q4 + 4j + i); those in [lo, L) are attended.  A page
-    // wholly inside [lo, L) (every page but the first and last of a slot)
+    // (FP8: key0 + 16q4 + 4j + i); those in [lo, Lq) are attended.  A page
+    // wholly inside [lo, Lq) (every page but the first and last of a slot)
     // takes the branch without masks.
-    float sv[4][4];
-    const bool interior = key0 >= lo && key0 + kPage <= Lq;   // uniform
-    if (interior) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int tk = 0; tk < kTps; ++tk) {
+      float sv[4][4];
+      const bool interior = key0 >= lo && key0 + kPage <= Lq[tk];   // uniform
+      if (interior) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[j][i] = st[j][i] * qk_scale;
-    } else {
-      const int ebase = key0 + (kMap16 ? 16 : 8) * q4;
-      const int e_lo = lo - ebase, e_hi = Lq - ebase;
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[j][i] = st[tk][j][i] * qk_scale;
+      } else {
+        const int ebase = key0 + (kMap16 ? 16 : 8) * q4;
+        const int e_lo = lo - ebase, e_hi = Lq[tk] - ebase;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = kMap16 ? 4 * j + i : 32 * (j >> 1) + 4 * (j & 1) + i;
+            sv[j][i] = (e >= e_lo && e < e_hi) ? st[tk][j][i] * qk_scale : kNegInf;
+          }
+      }
+      float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+#pragma unroll
+      for (int j = 1; j < 4; ++j)
+        mx = fmaxf(mx, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
+      mx = wave_max_xor16_32(mx);
+      // Lazy max: keep the old reference unless this tile exceeds it by > 2^8.
+      const bool move = mx > m_run[tk] + kLazyRescale;
+      const float m_new = move ? mx : m_run[tk];
+      if (__any(move && m_run[tk] != kNegInf)) {
+        const float alpha = fast_exp2(m_run[tk] - m_new);   // 1 where the max stays
+        l_run[tk] *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < kD / 16; ++ct) acc[tk][ct] *= alpha;
+      }
+      m_run[tk] = m_new;
+      // p = 2^(s - m); a head with no attended key yet (m = -inf, only on a
+      // masked page) gets p = 0 instead of 2^NaN.
+      const float m_sub = m_new == kNegInf ? 0.f : m_new;
+      float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = kMap16 ? 4 * j + i : 32 * (j >> 1) + 4 * (j & 1) + i;
-          sv[j][i] = (e >= e_lo && e < e_hi) ? st[j][i] * qk_scale : kNegInf;
+          sv[j][i] = fast_exp2(sv[j][i] - m_sub);
+          psum += sv[j][i];
         }
+      l_run[tk] += psum;
+      // P^T B operands: keys 32s + 8q4 .. +7 (FP8: 16q4 + 8s .. +7) come
+      // from tiles 2s (first four) and 2s + 1 (last four).
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        pb[tk][s] = intx4{(int)pack_bf16x2(sv[2 * s][0], sv[2 * s][1]), (int)pack_bf16x2(sv[2 * s][2], sv[2 * s][3]),
+                          (int)pack_bf16x2(sv[2 * s + 1][0], sv[2 * s + 1][1]),
+                          (int)pack_bf16x2(sv[2 * s + 1][2], sv[2 * s + 1][3])};
     }
-    float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
-#pragma unroll
-    for (int j = 1; j < 4; ++j)
-      mx = fmaxf(mx, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
-    mx = wave_max_xor16_32(mx);
-    // Lazy max: keep the old reference unless this tile exceeds it by > 2^8.
-    const bool move = mx > m_run + kLazyRescale;
-    const float m_new = move ? mx : m_run;
-    if (__any(move && m_run != kNegInf)) {
-      const float alpha = fast_exp2(m_run - m_new);   // 1 where the max stays
-      l_run *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < kD / 16; ++ct) acc[ct] *= alpha;
-    }
-    m_run = m_new;
-    // p = 2^(s - m); a head with no attended key yet (m = -inf, only on a
-    // masked page) gets p = 0 instead of 2^NaN.
-    const float m_sub = m_new == kNegInf ? 0.f : m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[j][i] = fast_exp2(sv[j][i] - m_sub);
-        psum += sv[j][i];
-      }
-    l_run += psum;
-    // P^T B operands: keys 32s + 8q4 .. +7 (FP8: 16q4 + 8s .. +7) come from
-    // tiles 2s (first four) and 2s + 1 (last four).
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      pb[s] = intx4{(int)pack_bf16x2(sv[2 * s][0], sv[2 * s][1]), (int)pack_bf16x2(sv[2 * s][2], sv[2 * s][3]),
-                    (int)pack_bf16x2(sv[2 * s + 1][0], sv[2 * s + 1][1]),
-                    (int)pack_bf16x2(sv[2 * s + 1][2], sv[2 * s + 1][3])};
   };
 
   auto v_phase = [&]() __attribute__((always_inline)) {
@@ -841,8 +928,13 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
       for (int ct = 0; ct < kD / 16; ++ct) raw[ct] = *reinterpret_cast<const intx4*>(vslot + vfrag0 + ct * 1024);
 #pragma unroll
       for (int ct = 0; ct < kD / 16; ++ct) {
-        acc[ct] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[ct].x, raw[ct].y), pb[0], acc[ct]);
-        acc[ct] = mfma_bf16_16x16x32(e4m3x8_to_bf16(raw[ct].z, raw[ct].w), pb[1], acc[ct]);
+        const intx4 v_lo = e4m3x8_to_bf16(raw[ct].x, raw[ct].y);
+        const intx4 v_hi = e4m3x8_to_bf16(raw[ct].z, raw[ct].w);
+#pragma unroll
+        for (int tk = 0; tk < kTps; ++tk) {
+          acc[tk][ct] = mfma_bf16_16x16x32(v_lo, pb[tk][0], acc[tk][ct]);
+          acc[tk][ct] = mfma_bf16_16x16x32(v_hi, pb[tk][1], acc[tk][ct]);
+        }
       }
       if constexpr (kTps == 1) {
         __builtin_amdgcn_sched_group_barrier(0x100, kAhead8, 0);
@@ -864,51 +956,47 @@ __global__ void __launch_bounds__(256 * kTps + kLoaders) mqa_decode_kernel(Decod
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = mfma_bf16_16x16x32(a[s][ct], pb[s], acc[ct]);
-    if constexpr (kTps == 1) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+      for (int ct = 0; ct < kD / 16; ++ct)
 #pragma unroll
-      for (int i = 0; i < 32 - kAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        for (int tk = 0; tk < kTps; ++tk) acc[tk][ct] = mfma_bf16_16x16x32(a[s][ct], pb[tk][s], acc[tk][ct]);
+    // Each V^T read feeds one product per token.
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 32 - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kTps, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kTps * kAhead, 0);
   };
 
   if constexpr (kBal) {
-    // Tiles back to back; the loaders stream straight across piece
-    // boundaries.  A new piece (slot) starts a fresh state on its query.
-    // Piece 0 of workgroup w is partial w, its last piece partial G + w
-    // (G workgroups).
-    int pg_first = 0, pg_last = 0, piece = 0;
-    for (int t = 0; t < nt; ++t) {
+    // Pieces back to back.  The tiles of one slot are consecutive pages, so
+    // a piece runs from its first tile up to the slot's last page or the end
+    // of the workgroup's range; the loaders stream straight across piece
+    // boundaries.  A new piece starts a fresh state on its query.  Piece 0
+    // of workgroup w is partial w, its last piece partial G + w (G
+    // workgroups); the pieces between are whole slots.
+    for (int t = 0, piece = 0; t < nt; ++piece) {
       const int info = readfirstlane(tile_pg[t]);
-      const int slot = info >> 20, page = info & 0xfffff;
-      if (t == 0) {
-        L = readfirstlane(bal_len[slot]);
-        Lq = query_keys(L);
-        pg_first = page;
-      } else if (slot != b) {
-        store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + wl);
-        ++piece;
+      const int slot = info >> 20, page0 = info & 0xfffff;
+      L = readfirstlane(bal_len[slot]);
+      const int pages = (L + kPage - 1) / kPage;
+      const int t_stop = min(nt, t + max(pages - page0, 1));
+      if (piece > 0) {
         b = slot;
-        load_q();
-        L = readfirstlane(bal_len[slot]);
-        Lq = query_keys(L);
-        pg_first = page;
-        m_run = kNegInf;
-        l_run = 0.f;
-#pragma unroll
-        for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+        load_q(b);
+        reset_state();
       }
-      pg_last = page;
-      lds_barrier();   // K tile visible
-      k_phase(page * kPage);
-      lds_barrier();   // V^T tile visible
-      v_phase();
+      set_query_keys(L);
+      const bool whole = page0 == 0 && t_stop - t == pages;
+      for (int key0 = page0 * kPage; t < t_stop; ++t, key0 += kPage) {
+        lds_barrier();   // K tile visible
+        k_phase(key0);
+        lds_barrier();   // V^T tile visible
+        v_phase();
+      }
+      store_result(whole, (piece > 0 ? (int64_t)gridDim.x : 0) + wl);
     }
-    store_result(pg_first == 0 && pg_last == (L + kPage - 1) / kPage - 1, (piece > 0 ? (int64_t)gridDim.x : 0) + wl);
     return;
   }
   for (int t = 0; t < nt; ++t) {
@@ -934,7 +1022,7 @@ constexpr bool kFp8K8 = true, kFp8V8 = false;
 
 template <int kTps>
 void launch_mqa_t(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream) {
-  const dim3 block(256 * kTps + kLoaders);
+  const dim3 block(256 + kLoaders);
   const dim3 grid(p.splits, p.batch * p.hkv);
   if (p.balanced) {
     // One workgroup per range of the batch's pages: as many as the split
