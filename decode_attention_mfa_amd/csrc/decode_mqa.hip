@@ -444,7 +444,6 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
       }
     } else {
       b = spec_b;
-      load_q(b);
       // Block ids of the split plan's pages for this workgroup, fetched
       // with the lengths (tile i = tid + kCt k); used where the partition
       // agrees.
@@ -464,11 +463,20 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
       // pages, scanned.
       int len[kSpt], pg[kSpt];
       int incl = 0;
+      int raw[kSpt];
+#pragma unroll
+      for (int k = 0; k < kSpt; ++k) raw[k] = query_len_flat(p, min(kSpt * tid + k, p.batch - 1));
+      // The query after the lengths: the wave's loads complete in order, and
+      // the scan needs only the lengths (kept out of a branch, where the
+      // compiler would wait for the query too).
+      asm volatile("" ::: "memory");
+      load_q(b);
+#pragma unroll
+      for (int k = 0; k < kSpt; ++k) asm volatile("" : "+v"(raw[k]));
 #pragma unroll
       for (int k = 0; k < kSpt; ++k) {
         const int sk = kSpt * tid + k;
-        const int raw = query_len(p, min(sk, p.batch - 1));
-        len[k] = sk < p.batch ? raw : 0;
+        len[k] = sk < p.batch ? raw[k] : 0;
         pg[k] = (len[k] + kPage - 1) / kPage;
         incl += pg[k];
       }

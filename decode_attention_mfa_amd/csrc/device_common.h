@@ -77,6 +77,16 @@ __device__ __forceinline__ int query_len(const P& p, int s) {
   const int last = (s - seq * per_seq) * p.tps + p.tps - 1;
   return max(slot_len(p.ctx_lens[seq], p.max_blocks) - (p.tq - 1 - last), 0);
 }
+// The same without control flow, for per-lane slots: the compiler waits for
+// every earlier load of the wave where the branches of the form above join
+// (tq = 1 implies tps = 1, where the general form reduces to the length).
+template <class P>
+__device__ __forceinline__ int query_len_flat(const P& p, int s) {
+  const int per_seq = p.tq / p.tps;
+  const int seq = s / per_seq;
+  const int last = (s - seq * per_seq) * p.tps + p.tps - 1;
+  return max(slot_len(p.ctx_lens[seq], p.max_blocks) - (p.tq - 1 - last), 0);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
