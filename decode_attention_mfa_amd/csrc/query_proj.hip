@@ -50,7 +50,7 @@ constexpr int kStages = 4;                 // ring depth
 // waits on LDS or the barrier.
 constexpr int kKGroups = 2;
 constexpr int kThreads = 256 * kKGroups;
-constexpr int kNormThreads = 256;
+constexpr int kNormThreads = 512;
 constexpr int kRowBytes = kStepK * 2;
 constexpr int kChunksPerRow = kRowBytes / 16;
 constexpr int kRowsPerLine = 128 / kRowBytes;                // rows sharing a 128-byte line
@@ -235,34 +235,37 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 }
 
 // One workgroup per row: sum the split-K partials in split order, RMS-normalise,
-// apply the gain and write r in bf16.  Each thread owns groups of four
-// consecutive columns; every partial of a group is loaded before any is added.
+// apply the gain and write r in bf16.  Each thread owns kGroups groups of four
+// consecutive columns (kGroups = 1 up to rank 2048, else 2).  Every load is
+// issued before any is used: indices are clamped into range and the extra
+// splits and columns masked, since a load inside a branch makes the compiler
+// wait for each one in turn (one memory round trip per split).
+template <int kGroups>
 __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(const float* __restrict__ y_part,
                                                             int k_splits, int batch, int rank,
                                                             float eps,
                                                             const float* __restrict__ gain,
                                                             uint16_t* __restrict__ r_out) {
-  constexpr int kGroups = 4096 / 4 / kNormThreads;   // rank <= 4096
   const int b = blockIdx.x;
+  floatx4 part[kGroups][kMaxQueryKSplits], gn[kGroups];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int cc = min(4 * (g * kNormThreads + (int)threadIdx.x), rank - 4);
+#pragma unroll
+    for (int s = 0; s < kMaxQueryKSplits; ++s)
+      part[g][s] = *reinterpret_cast<const floatx4*>(y_part + ((size_t)min(s, k_splits - 1) * batch + b) * rank + cc);
+    gn[g] = gain ? *reinterpret_cast<const floatx4*>(gain + cc) : floatx4{1.f, 1.f, 1.f, 1.f};
+  }
   floatx4 y[kGroups];
   float ss = 0.f;
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
-    const int c = 4 * (g * kNormThreads + threadIdx.x);
-    floatx4 part[kMaxQueryKSplits];
+    floatx4 v = part[g][0];
 #pragma unroll
-    for (int s = 0; s < kMaxQueryKSplits; ++s) {
-      part[s] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (c < rank && s < k_splits)
-        part[s] = *reinterpret_cast<const floatx4*>(y_part + ((size_t)s * batch + b) * rank + c);
-    }
-    floatx4 v = part[0];
+    for (int s = 1; s < kMaxQueryKSplits; ++s) v += s < k_splits ? part[g][s] : floatx4{0.f, 0.f, 0.f, 0.f};
+    y[g] = 4 * (g * kNormThreads + (int)threadIdx.x) < rank ? v : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 1; s < kMaxQueryKSplits; ++s)
-      if (s < k_splits) v += part[s];
-    y[g] = v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ss += v[e] * v[e];
+    for (int e = 0; e < 4; ++e) ss += y[g][e] * y[g][e];
   }
   __shared__ float red[kNormThreads / 64];
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(const float* __r
     ushortx4 h;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float r = y[g][e] * inv * (gain ? gain[c + e] : 1.0f);
+      const float r = y[g][e] * inv * gn[g][e];
       h[e] = __builtin_bit_cast(uint16_t, (__bf16)r);
     }
     *reinterpret_cast<ushortx4*>(r_out + (size_t)b * rank + c) = h;
@@ -305,8 +308,12 @@ mfa_status query_proj_enqueue(const mfa_query_proj_desc* d, const QueryProjPlan&
                        static_cast<const uint16_t*>(x), H, static_cast<const uint16_t*>(w_down), H,
                        B, R, m_tiles, n_tiles, H / pl.k_splits, y_part, R, (size_t)B * R);
   }
-  hipLaunchKernelGGL(rms_norm_kernel, dim3(B), dim3(kNormThreads), 0, stream, y_part, pl.k_splits, B,
-                     R, d->eps, gain, r);
+  if (R > 4 * kNormThreads)
+    hipLaunchKernelGGL(rms_norm_kernel<2>, dim3(B), dim3(kNormThreads), 0, stream, y_part, pl.k_splits, B,
+                       R, d->eps, gain, r);
+  else
+    hipLaunchKernelGGL(rms_norm_kernel<1>, dim3(B), dim3(kNormThreads), 0, stream, y_part, pl.k_splits, B,
+                       R, d->eps, gain, r);
   {
     const int n_tiles = (N + kTile - 1) / kTile;
     dim3 grid(m_tiles * n_tiles);
