@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(256) combine_balanced_kernel(DecodeParams p) {
   const int b = (int)(row / p.hq);
   const int h = (int)(row - (int64_t)b * p.hq);
   const int S = p.splits;
-  const int L = query_len(p, b);
+  const int L = query_len_flat(p, b);   // (no branch: its load goes out with the others)
   const intx4 dsc = *reinterpret_cast<const intx4*>(p.unit_desc + 4 * (int64_t)b);
   floatx2 ml[kMaxSplits];
   vec o[kMaxSplits];
