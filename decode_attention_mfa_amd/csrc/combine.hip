@@ -11,9 +11,10 @@
 //
 // O_c is stored in fp32 in channel order, or, when the call's result is bf16
 // (the shared-tile MQA kernel, d = 256), rounded to bf16 with each group of
-// 32 channels stored as four 8-element runs: run r of group j holds channels
-// 32j + 4r .. +3, then 32j + 16 + 4r .. +3.  The producing wave then writes
-// 64 contiguous bytes per head with each store.  m_c and l_c stay fp32.
+// 32 channels stored as four 8-element runs: run q of group j holds channels
+// 32j + 4q .. +3, then 32j + 16 + 4q .. +3.  Rows go in pairs: group j of
+// rows 2i and 2i+1 shares one 128-byte line (row 2i first), so each store of
+// the producing wave writes whole lines.  m_c and l_c stay fp32.
 //
 // fp32 partials: one wave per (slot, head), lane l owns channels 4l .. 4l+3.
 // bf16 partials: one wave per two rows, lane l owns run l % 32 of row l / 32.
@@ -57,14 +58,19 @@ struct MergeLane<false> {
 };
 
 template <>
-struct MergeLane<true> {   // d = 256
+struct MergeLane<true> {   // d = 256, bf16 partials and a bf16 result
   using vec = floatx8;
   static constexpr int kRowsPerWave = 2;
   int run;
   bool live = true;
   __device__ MergeLane(int lane, int) : run(lane & 31) {}
+  // Run 4j + q of row r sits in the lines of the row pair (r & ~1), at
+  // 64 j + 32 (r & 1) + 8 q elements: a wave merging rows 2i, 2i+1 reads
+  // one contiguous kilobyte per partial.
   __device__ vec load(const DecodeParams& p, int64_t r, int) const {
-    const intx4 h = *reinterpret_cast<const intx4*>(reinterpret_cast<const uint16_t*>(p.part_o) + r * 256 + run * 8);
+    const intx4 h = *reinterpret_cast<const intx4*>(reinterpret_cast<const uint16_t*>(p.part_o) +
+                                                    (r & ~(int64_t)1) * 256 + (run >> 2) * 64 +
+                                                    (r & 1) * 32 + (run & 3) * 8);
     vec v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -73,10 +79,23 @@ struct MergeLane<true> {   // d = 256
     }
     return v;
   }
+  // The lane holds channels 32j + 4q .. +3 (v[0..3]) and 32j + 16 + 4q ..
+  // +3 (v[4..7]) of run 4j + q.  The four lanes of a run group (one lane
+  // quad) trade halves so that lane q stores the 8 consecutive channels
+  // 32j + 8q .. +7: lanes 2(q & 1) and 2(q & 1) + 1 of the quad supply their
+  // low halves (q < 2) or their high halves (q >= 2).  A row is then 32
+  // stores of 16 bytes, four whole lines, streamed out.
   __device__ void store(const DecodeParams& p, int64_t out_row, vec v) const {
-    const int c0 = 32 * (run >> 2) + 4 * (run & 3);
-    store_out4(p, out_row + c0, floatx4{v[0], v[1], v[2], v[3]});
-    store_out4(p, out_row + c0 + 16, floatx4{v[4], v[5], v[6], v[7]});
+    const int lo0 = (int)pack_bf16x2(v[0], v[1]), lo1 = (int)pack_bf16x2(v[2], v[3]);
+    const int hi0 = (int)pack_bf16x2(v[4], v[5]), hi1 = (int)pack_bf16x2(v[6], v[7]);
+    const int q = run & 3;
+    const int src0 = (int)(threadIdx.x & 60) | ((q & 1) << 1);
+    const int src1 = src0 + 1;
+    const int a0 = __shfl(lo0, src0), a1 = __shfl(lo1, src0), a2 = __shfl(lo0, src1), a3 = __shfl(lo1, src1);
+    const int b0 = __shfl(hi0, src0), b1 = __shfl(hi1, src0), b2 = __shfl(hi0, src1), b3 = __shfl(hi1, src1);
+    const intx4 w = q < 2 ? intx4{a0, a1, a2, a3} : intx4{b0, b1, b2, b3};
+    __builtin_nontemporal_store(
+        w, reinterpret_cast<intx4*>(static_cast<uint16_t*>(p.out) + out_row + 32 * (run >> 2) + 8 * q));
   }
 };
 

@@ -647,19 +647,19 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
       // Split partials are read once, by the merge kernel.
       const int64_t row = piece * kRows + ((id.head + tk * kG) - g * kRows);
       if (p.part_bf16) {
-        // bf16 rows: tiles 2j and 2j+1 of this lane form run 4j + q4 (8
-        // elements), so the four q4 lanes of a head write 64 contiguous
-        // bytes.  Plain stores: L2 joins the two 64-byte halves of each line
-        // (streamed out, the halves left separately: 12.2 MB written for
-        // 8.4 MB).
-        uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + row * kD + id.q4 * 8;
+        // bf16 rows, stored by row pairs: tiles 2j and 2j+1 of this lane
+        // form run 4j + q4 (8 elements), and the runs 4j .. 4j+3 of rows 2i
+        // and 2i+1 (the lanes of heads r and r ^ 1) fill one 128-byte line,
+        // so every store of the wave writes whole lines, streamed out.
+        uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + (row & ~(int64_t)1) * kD + (row & 1) * 32 + id.q4 * 8;
 #pragma unroll
         for (int j = 0; j < kD / 32; ++j)
-          *reinterpret_cast<intx4*>(po + j * 32) =
+          __builtin_nontemporal_store(
               intx4{(int)pack_bf16x2(acc[tk][2 * j].x, acc[tk][2 * j].y),
                     (int)pack_bf16x2(acc[tk][2 * j].z, acc[tk][2 * j].w),
                     (int)pack_bf16x2(acc[tk][2 * j + 1].x, acc[tk][2 * j + 1].y),
-                    (int)pack_bf16x2(acc[tk][2 * j + 1].z, acc[tk][2 * j + 1].w)};
+                    (int)pack_bf16x2(acc[tk][2 * j + 1].z, acc[tk][2 * j + 1].w)},
+              reinterpret_cast<intx4*>(po + j * 64));
       } else {
         // fp32 rows (whole 64-byte quarters of a line per store): streamed
         // out rather than kept dirty in L2 for the write-back at the
