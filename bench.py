@@ -146,6 +146,33 @@ def committed_counters(config):
         return None, None
 
 
+def stream_read_rate(nbytes, steps, warmup, stream):
+    """Time mfa_stream_read over nbytes (rounded down to whole 16-byte loads):
+    the read rate a kernel with no other work reaches on this GPU."""
+    import torch
+    import decode_attention_mfa_amd as mfa
+    n = (int(nbytes) // 16) * 4
+    bufs = [torch.full((n,), i + 1, dtype=torch.int32, device="cuda") for i in range(4)]
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.int32, device="cuda")
+    for i in range(max(warmup, 4)):
+        mfa.mfa_stream_read(bufs[i % 4], sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        mfa.mfa_stream_read(bufs[i % 4], sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del bufs
+    return {"achieved": n * 4 / us * 1e-3, "unit": "GB/s", "us": us, "bytes": n * 4,
+            "frac_of_peak": n * 4 / us * 1e-3 / HBM_PEAK_GBPS,
+            "timed": "mfa_stream_read (16-byte non-temporal loads, one workgroup per compute "
+                     "unit) over the call's algorithmic bytes, K back-to-back launches under "
+                     "one event pair"}
+
+
 def copy_calibration(steps):
     """A plain device-to-device copy of a known size (1 GiB per dispatch), run
     under rocprofv3 --pmc to scale the FETCH_SIZE / WRITE_SIZE counters."""
@@ -599,6 +626,14 @@ def main():
     splits = mfa.mfa_decode_plan_splits(desc, window,
                                         torch.cuda.get_device_properties(dev).multi_processor_count)
 
+    # The read rate of a kernel that only streams, measured in the same run:
+    # the library's plain streaming-read kernel over the call's algorithmic
+    # byte count (the attention's, for config 4), K back-to-back launches
+    # under one event pair, rotating over four buffers like the pool copies.
+    # A practical reference below the published peak, not a bound: the
+    # per-group kernel matches it on the 32K global layer.
+    stream_ref = stream_read_rate(nbytes, args.steps, args.warmup, stream)
+
     counters = committed_counters(args.config) if not args.with_append else (None, None)
     if qpath is not None:
         nbytes += qpath_res["bytes"]
@@ -656,6 +691,9 @@ def main():
                               "merge kernel per step" + (", after the KV append)" if
                                                         args.with_append else ")"))},
     }
+    res["roofline"]["stream_read"] = dict(
+        stream_ref, kernel_frac=(kernel_achieved / stream_ref["achieved"]) if kernel_achieved else None,
+        step_frac=achieved / stream_ref["achieved"] if qpath is None else None)
     if qpath_res is not None:
         res["query_path"] = qpath_res
     if not args.no_cpu_baseline:

@@ -17,6 +17,7 @@ from .binding import (
     mfa_sparse_select,
     mfa_sparse_summarize,
     mfa_sparse_summarize_new,
+    mfa_stream_read,
     V_LAYOUTS,
 )
 
@@ -35,5 +36,6 @@ __all__ = [
     "mfa_sparse_select",
     "mfa_sparse_summarize",
     "mfa_sparse_summarize_new",
+    "mfa_stream_read",
     "V_LAYOUTS",
 ]

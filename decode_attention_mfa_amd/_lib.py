@@ -36,6 +36,7 @@ EXPORTED = (
     "mfa_sparse_select",
     "mfa_sparse_attention",
     "mfa_sparse_workspace_size",
+    "mfa_stream_read",
     "mfa_status_string",
     "mfa_abi_version",
 )
@@ -136,6 +137,8 @@ def load():
     lib.mfa_decode_workspace_size.restype = ctypes.c_size_t
     lib.mfa_decode_plan_splits.argtypes = [desc_p, ctypes.c_int32, ctypes.c_int32]
     lib.mfa_decode_plan_splits.restype = ctypes.c_int32
+    lib.mfa_stream_read.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t, P]
+    lib.mfa_stream_read.restype = ctypes.c_int
     lib.mfa_kv_append.argtypes = [ctypes.POINTER(MfaKvAppendDesc), P, P, P, P, P, P, P, P, P, P]
     lib.mfa_kv_append.restype = ctypes.c_int
     lib.mfa_kv_append_layout.argtypes = [ctypes.POINTER(MfaKvAppendDesc), P, P, P, P, P, P, P, P,

@@ -336,3 +336,15 @@ def mfa_query_proj(x, w_qdown, w_qup, q_out, *, num_heads=64, gain=None, eps=1e-
                              _ptr(gain), _ptr(q_out), _ptr(ws), ctypes.c_size_t(ws_bytes),
                              _stream(x, stream)))
     return q_out
+
+
+def mfa_stream_read(src, sink, *, stream=None):
+    """Read-rate reference: streams every byte of the CUDA tensor `src` once
+    (see mfa_stream_read in the header); `sink` is an int32 CUDA tensor of at
+    least num_cus * 512 entries, whose XOR equals the XOR of src's words."""
+    lib = _lib.load()
+    if sink.dtype != torch.int32:
+        raise TypeError("sink must be int32")
+    check(lib.mfa_stream_read(_ptr(src), ctypes.c_size_t(src.numel() * src.element_size()),
+                              _ptr(sink), ctypes.c_size_t(sink.numel()), _stream(src, stream)))
+    return sink

@@ -15,6 +15,9 @@ hipError_t launch_gqa(const DecodeParams& p, int d, bool fp8, hipStream_t stream
 hipError_t launch_f32(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, int group, int d, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, int new_dtype, int kv_dtype, hipStream_t stream);
+int stream_read_threads();
+hipError_t launch_stream_read(const void* src, int64_t bytes, int32_t* sink, int workgroups,
+                              hipStream_t stream);
 mfa_status query_proj_enqueue(const mfa_query_proj_desc* d, const QueryProjPlan& pl,
                               const void* x, const void* w_down, const void* w_up,
                               const float* gain, void* q_out, void* workspace,
@@ -352,6 +355,20 @@ mfa_status mfa_query_proj(const mfa_query_proj_desc* desc, const void* x, const 
 size_t mfa_query_proj_workspace_size(const mfa_query_proj_desc* desc) {
   if (mfa::validate_query_proj_desc(desc) != MFA_OK) return 0;
   return mfa::plan_query_proj(desc).workspace_bytes;
+}
+
+mfa_status mfa_stream_read(const void* src, size_t bytes, int32_t* sink, size_t sink_len,
+                           mfa_stream_t stream) {
+  if (!src || !sink) return MFA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(src) & 15u) return MFA_ERR_ALIGN;
+  if (bytes == 0 || bytes % 16 || bytes > ((size_t)1 << 40)) return MFA_ERR_SHAPE;
+  const int wgs = device_cu_count();
+  if (wgs <= 0) return MFA_ERR_LAUNCH;
+  if (sink_len < (size_t)wgs * (size_t)mfa::stream_read_threads()) return MFA_ERR_SHAPE;
+  return mfa::launch_stream_read(src, (int64_t)bytes, sink, wgs, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MFA_OK
+             : MFA_ERR_LAUNCH;
 }
 
 const char* mfa_status_string(mfa_status s) {

@@ -478,6 +478,28 @@ mfa_status mfa_sparse_attention(const mfa_sparse_desc* desc, const void* q, cons
  * of the scores and the attention's split partials; 0 for a bad desc). */
 size_t mfa_sparse_workspace_size(const mfa_sparse_desc* desc);
 
+/*
+ * Read-rate reference (measurement only; not part of a decode call).  Reads
+ * the `bytes` bytes at `src` once, the way the decode kernels stream their
+ * tiles: 16-byte non-temporal loads, the buffer cut into one contiguous
+ * range per workgroup, one workgroup of 512 threads per compute unit.  Timed
+ * over a decode call's byte count, it gives the read rate a kernel with no
+ * other work reaches on this device: a practical reference below the
+ * published HBM peak for the memory-bound MFA decode ("Step-3 is Large yet
+ * Affordable", section 5.1), not a bound (a kernel with more bytes in flight
+ * can match or pass it).
+ *   src       device memory, 16-byte aligned; bytes > 0, a multiple of 16
+ *   sink      int32 [sink_len] device memory; sink_len >= num_cus * 512,
+ *             where num_cus is the current device's compute-unit count.
+ *             Thread t of workgroup w writes sink[512 w + t] = the XOR of
+ *             every 32-bit word it read, so the XOR of sink[0 .. 512 num_cus)
+ *             equals the XOR of all 32-bit words of the buffer.
+ * Enqueues one kernel on `stream`; errors as for the decode calls (NULL
+ * pointers MFA_ERR_NULL, misaligned src MFA_ERR_ALIGN, sizes MFA_ERR_SHAPE).
+ */
+mfa_status mfa_stream_read(const void* src, size_t bytes, int32_t* sink, size_t sink_len,
+                           mfa_stream_t stream);
+
 /* Static, never-NULL description of a status code. */
 const char* mfa_status_string(mfa_status status);
 

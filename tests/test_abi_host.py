@@ -315,3 +315,19 @@ def test_binding_checks_the_sub_blocked_v_shape():
     with pytest.raises(ValueError, match="v_layout"):
         mfa.mfa_decode_attention_gqa(q, k, v_channel, table, lens, out, 0.07, num_splits=1,
                                      v_layout="tokens")
+
+
+def test_stream_read_rules():
+    """The read-rate reference validates before it launches: NULL pointers,
+    a misaligned source and byte counts that are zero or not whole 16-byte
+    loads are refused on the host."""
+    lib = _lib.load()
+
+    def call(src, nbytes, sink, sink_len):
+        return lib.mfa_stream_read(src, ctypes.c_size_t(nbytes), sink, ctypes.c_size_t(sink_len),
+                                   None)
+    assert call(None, 1 << 20, A, 1 << 20) == MFA_ERR_NULL
+    assert call(A, 1 << 20, None, 1 << 20) == MFA_ERR_NULL
+    assert call(ctypes.c_void_p(0x10008), 1 << 20, A, 1 << 20) == MFA_ERR_ALIGN
+    assert call(A, 0, A, 1 << 20) == MFA_ERR_SHAPE
+    assert call(A, (1 << 20) + 8, A, 1 << 20) == MFA_ERR_SHAPE
