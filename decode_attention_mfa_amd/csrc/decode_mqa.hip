@@ -30,12 +30,15 @@
 // reduced once at the end; a compute wave holds all keys of its heads, so
 // its output (or split partial) is final without any merge between waves.
 //
-// FP8 E4M3 caches stay 8-bit in LDS (K rows of 256 B, V^T rows of 64 B) and
-// are widened to bf16 in registers after the read.  The MFMA k-index <->
-// channel and row <-> key maps are chosen so that one 16-byte LDS read of a
-// lane holds the operands of two products: QK^T step c takes channels
-// 64(c/2) + 16(l/16) + 8(c%2) + e, S^T row r of tile j is key
-// 16(r/4) + 4j + r%4, and PV step s takes keys 16(l/16) + 8s + e.
+// FP8 E4M3 caches stay 8-bit in LDS (K rows of 256 B, V^T rows of 64 B).
+// Single-token slots form S^T on the E4M3 matrix unit straight from the
+// 8-bit K rows, with the query split exactly into two E4M3 terms (below);
+// token pairs and V^T operands are widened to bf16 in registers after the
+// read.  The MFMA k-index <-> channel and row <-> key maps are chosen so
+// that one 16-byte LDS read of a lane holds the operands of two bf16
+// products: QK^T step c takes channels 64(c/2) + 16(l/16) + 8(c%2) + e,
+// S^T row r of tile j is key 16(r/4) + 4j + r%4, and PV step s takes keys
+// 16(l/16) + 8s + e.
 //
 // Multi-token queries ("Step-3 is Large yet Affordable", section 5.2, MTP):
 // a call with tq new tokens per cached sequence runs B * tq query slots;
@@ -191,6 +194,11 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
   static_assert(kSpt * kCt == kMaxBalancedSlots && kTpt * kCt == kMaxBalancedTiles &&
                 kMaxBalancedTiles <= kMaxChunkTiles, "slots and tiles split evenly over compute threads");
   constexpr bool kMap16 = kK8;                          // key map of 8-bit K tiles
+  // 8-bit K tiles of single-token slots multiply on the E4M3 matrix unit;
+  // token pairs widen them to bf16 (their two tokens' accumulators leave no
+  // registers for the split query's fragments: the E4M3 form spilled in
+  // the tile loop and ran 55 % slower).
+  constexpr bool kE4m3 = kK8 && kTps == 1;
   constexpr int kElem = kFp8 ? 1 : 2;                 // bytes per cached element
   constexpr int kPerThread = kPhaseBytes * kElem / 2 / 16 / kLoaders;   // 16-byte loads per phase
   constexpr int kKSlot = kK8 ? kPhaseBytes / 2 : kPhaseBytes;   // LDS bytes of a K tile
@@ -383,7 +391,22 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
   // +7 (FP8: 64(c/2) + 16q4 + 8(c%2) .. +7).  With token pairs each compute
   // wave parks both tokens' fragments in its own LDS rows and reads them
   // back per K tile, so that they are not held across the V phase.
+  //
+  // Single-token slots over 8-bit K tiles (kE4m3) multiply on the E4M3
+  // matrix unit instead: the 16x16x128 product pairs byte i of lane group
+  // l/16 in both operands, so
+  // lane (r, q4) takes channels 128m + 32q4 .. +31 of K row and query for
+  // product m = 0, 1.  The query of a head is scaled by a power of two
+  // 2^e (its largest magnitude below 256) and split into two E4M3 terms,
+  // hi = E4M3(2^e q) and lo = E4M3(2^e q - hi): a bf16 value has 8
+  // significant bits and each term holds 4, so hi + lo is 2^e q exactly
+  // for elements down to ~2^-10 of the head's largest; below that lo is
+  // rounded to the E4M3 subnormal step 2^-9, an error under 2^-17 of the
+  // largest element.  S^T = K.hi + K.lo, descaled by 2^-e with the logit
+  // scale.  Fragment c = 4m + 2t + h holds term t (hi, lo), bytes
+  // 16h .. 16h + 15 of product m's 32 channels.
   intx4 qf[kD / 32];
+  float q_descale[kTps] = {};
   auto load_q = [&](int slot) __attribute__((always_inline)) {
     const LaneIds id = lane_ids();
 #pragma unroll
@@ -391,8 +414,48 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
       const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((int64_t)slot * p.hq + id.head + tk * kG) * kD;
 #pragma unroll
       for (int c = 0; c < kD / 32; ++c) {
-        const int ch = kMap16 ? 64 * (c >> 1) + 16 * id.q4 + 8 * (c & 1) : 32 * c + 8 * id.q4;
+        const int ch = kE4m3 ? 128 * (c >> 2) + 32 * id.q4 + 8 * (c & 3)
+                             : kMap16 ? 64 * (c >> 1) + 16 * id.q4 + 8 * (c & 1) : 32 * c + 8 * id.q4;
         qf[c] = *reinterpret_cast<const intx4*>(qp + ch);
+      }
+      if constexpr (kE4m3) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < kD / 32; ++c)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_lo_to_f32((uint32_t)qf[c][w])), fabsf(bf16_hi_to_f32((uint32_t)qf[c][w]))));
+        amax = wave_max_xor16_32(amax);   // the four lanes of this head
+        int ex = 0;
+        frexpf(amax, &ex);                // amax < 2^ex
+        const int sh = amax > 0.f ? min(max(8 - ex, -100), 100) : 0;
+        const float up = ldexpf(1.f, sh);
+        q_descale[tk] = ldexpf(1.f, -sh);
+        intx4 t8[kD / 32];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {   // 8 channels 128m + 32q4 + 8c .. +7
+            int hi[2], lo[2];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const float x0 = bf16_lo_to_f32((uint32_t)qf[4 * m + c][w]) * up;
+              const float x1 = bf16_hi_to_f32((uint32_t)qf[4 * m + c][w]) * up;
+              const int h2 = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+              const floatx2 hv = __builtin_amdgcn_cvt_pk_f32_fp8(h2, false);
+              const int l2 = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - hv.x, x1 - hv.y, 0, false);
+              const int sh16 = 16 * (w & 1);
+              if ((w & 1) == 0) { hi[w >> 1] = h2 & 0xffff; lo[w >> 1] = l2 & 0xffff; }
+              else { hi[w >> 1] |= (h2 & 0xffff) << sh16; lo[w >> 1] |= (l2 & 0xffff) << sh16; }
+            }
+            // term t, half h = c / 2 of product m: dwords 2 (c % 2) .. +1
+            t8[4 * m + 0 + (c >> 1)][2 * (c & 1)] = hi[0];
+            t8[4 * m + 0 + (c >> 1)][2 * (c & 1) + 1] = hi[1];
+            t8[4 * m + 2 + (c >> 1)][2 * (c & 1)] = lo[0];
+            t8[4 * m + 2 + (c >> 1)][2 * (c & 1) + 1] = lo[1];
+          }
+#pragma unroll
+        for (int c = 0; c < kD / 32; ++c) qf[c] = t8[c];
       }
       if constexpr (kTps == 2) {
 #pragma unroll
@@ -750,10 +813,11 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
   // whose swizzle is r itself; fragment c (channels 32c + 8q4 .. +7) is
   // chunk (4c + q4) ^ r = 4c ^ (q4 ^ r), at byte (kfrag ^ (c << 6)) +
   // 512 (32(j/2) + 4(j%2)).
-  // FP8: row r of tile j is key 16(r/4) + 4j + r%4 (swizzle r again); code
-  // chunk 4u + q4 holds the operands of steps 2u and 2u + 1, at byte
-  // (kfrag ^ (u << 6)) + 1024 j.
-  const uint32_t kfrag = kK8 ? (16 * (r >> 2) + (r & 3)) * 256 + ((q4 ^ r) << 4)
+  // FP8: row r of tile j is key 16(r/4) + 4j + r%4 (swizzle r again); the
+  // 32 codes of product m are chunks (8m + 2q4 + h) ^ r, h = 0, 1, at byte
+  // (kfrag ^ ((8m + h) << 4)) + 1024 j (the chunk bits of 8m, 2q4 and h do
+  // not overlap, so the sum is an XOR).
+  const uint32_t kfrag = kK8 ? (16 * (r >> 2) + (r & 3)) * 256 + (((kE4m3 ? 2 * q4 : q4) ^ r) << 4)
                              : (8 * (r >> 2) + (r & 3)) * 512 + ((q4 ^ r) << 4);
   // V^T operand of channel tile t, key step s: row 16t + r, chunk
   // (4s + q4) ^ swz_v(r) (8-bit K map: 2q4 + s), at byte vfrag_s + 2048 t.
@@ -777,7 +841,40 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
     for (int tk = 0; tk < kTps; ++tk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[tk][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (kK8) {
+    if constexpr (kE4m3) {
+      // Product m of S^T tile j: A = K row (32 codes: chunks 8m + 2q4 and
+      // 8m + 2q4 + 1 of the row), B = the query's hi and lo terms (two
+      // products into one accumulator).
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        intx4 raw[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            raw[j][h] = *reinterpret_cast<const intx4*>(kslot + (kb ^ ((8 * m + h) << 4)) + j * 1024);
+        const intx8 qhi = {qf[4 * m].x, qf[4 * m].y, qf[4 * m].z, qf[4 * m].w,
+                           qf[4 * m + 1].x, qf[4 * m + 1].y, qf[4 * m + 1].z, qf[4 * m + 1].w};
+        const intx8 qlo = {qf[4 * m + 2].x, qf[4 * m + 2].y, qf[4 * m + 2].z, qf[4 * m + 2].w,
+                           qf[4 * m + 3].x, qf[4 * m + 3].y, qf[4 * m + 3].z, qf[4 * m + 3].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const intx8 a = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
+                           raw[j][1].x, raw[j][1].y, raw[j][1].z, raw[j][1].w};
+          st[0][j] = mfma_e4m3_16x16x128(a, qhi, st[0][j]);
+          st[0][j] = mfma_e4m3_16x16x128(a, qlo, st[0][j]);
+        }
+        // Per product m: the first row's two reads, then two products
+        // behind each further row's reads.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    } else if constexpr (kK8) {
       intx4 raw[kD / 64][4];
       intx4 qv[kD / 64][kTps][2];   // token pairs: Q fragments read back per K tile
 #pragma unroll
@@ -875,12 +972,13 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
 #pragma unroll
     for (int tk = 0; tk < kTps; ++tk) {
       float sv[4][4];
+      const float qs = kE4m3 ? qk_scale * q_descale[tk] : qk_scale;   // (E4M3 products: the query's 2^-e)
       const bool interior = key0 >= lo && key0 + kPage <= Lq[tk];   // uniform
       if (interior) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sv[j][i] = st[tk][j][i] * qk_scale;
+          for (int i = 0; i < 4; ++i) sv[j][i] = st[tk][j][i] * qs;
       } else {
         const int ebase = key0 + (kMap16 ? 16 : 8) * q4;
         const int e_lo = lo - ebase, e_hi = Lq[tk] - ebase;
@@ -889,7 +987,7 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = kMap16 ? 4 * j + i : 32 * (j >> 1) + 4 * (j & 1) + i;
-            sv[j][i] = (e >= e_lo && e < e_hi) ? st[tk][j][i] * qk_scale : kNegInf;
+            sv[j][i] = (e >= e_lo && e < e_hi) ? st[tk][j][i] * qs : kNegInf;
           }
       }
       float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));

@@ -26,6 +26,18 @@ __device__ __forceinline__ floatx4 mfma_bf16_16x16x32(intx4 a, intx4 b, floatx4 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(8))) int intx8;
+
+// D(16x16 fp32) += A(16x128 E4M3) * B(128x16 E4M3) on the gfx950 8-bit
+// matrix unit (unit block scales: exponent code 127 = 2^0).  Lane l holds
+// row (A) / column (B) l % 16 and 32 K-indices; byte i of lane group l / 16
+// in A meets byte i of the same lane group in B, so any assignment of K
+// indices to (l / 16, i) shared by both operands gives the same product.
+// Result: lane l holds D[4*(l/16)+i][l%16], i = 0..3.
+__device__ __forceinline__ floatx4 mfma_e4m3_16x16x128(intx8 a, intx8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // Round-to-nearest-even fp32 -> bf16 of two values packed low/high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};

@@ -1,5 +1,6 @@
 """GPU parity of MFA decode attention over an FP8 E4M3 cache (per-KV-head fp32
-scales, codes converted to bf16 on the way to LDS) against the fp64 oracle.
+scales; single-token slots multiply K on the E4M3 matrix unit against a split
+query, token pairs widen K to bf16) against the fp64 oracle.
 
 Covers ragged lengths with NaN tail codes, every split count, fp32 output, the
 contiguous cache, the windowed path, the full-size 256 x 4096 batch on
@@ -12,7 +13,7 @@ import torch
 
 import decode_attention_mfa_amd as mfa
 from oracle import decode_attention
-from workloads import make_decode_case
+from workloads import bf16_round_bits, make_decode_case
 from workloads.device_gen import make_device_case
 
 from gpu_helpers import assert_parity, run_decode, to_device
@@ -53,6 +54,28 @@ def test_fp8_window(window):
     for splits in (0, 3):
         got = run_decode(case, t, num_splits=splits)
         assert_parity(got, oracle(case), "e4m3", f"fp8 window={window} splits={splits}")
+
+
+def test_fp8_query_dynamic_range():
+    """Single-token slots over an E4M3 cache form S^T on the 8-bit matrix unit
+    with each head's query scaled by a power of two and split into two E4M3
+    terms.  Queries whose elements span 2^-20 .. 1 of one another (below
+    ~2^-10 of a head's largest element the low term loses bits), heads
+    scaled from 2^-12 to 2^3, a head of zeros and a head with a single
+    non-zero element still meet the bar on every slot."""
+    case = make_decode_case(95, batch=3, ctx_lens=[700, 64, 2049], hq=64, hkv=1, d=256,
+                            kv_format="e4m3", scale=1 / 16)
+    rng = np.random.default_rng(95)
+    q = (case.q.astype(np.uint32) << 16).view(np.float32).reshape(case.batch, 64, 256).copy()
+    q *= np.exp2(rng.integers(-20, 1, size=q.shape)).astype(np.float32)
+    q[:, 20:36, :] *= np.exp2(np.arange(-12, 4)).astype(np.float32)[None, :, None]
+    q[:, 5, :] = 0.0
+    q[:, 9, :] = 0.0
+    q[:, 9, 17] = 3.0
+    case.q = bf16_round_bits(q)
+    for splits in (0, 3):
+        got = run_decode(case, to_device(case), num_splits=splits)
+        assert_parity(got, oracle(case), "e4m3", f"fp8 query range splits={splits}", per_slot=True)
 
 
 @pytest.mark.parametrize("jstar,splits", [(0, 1), (77, 0), (1000, 3), (1999, 4)])
