@@ -333,15 +333,29 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
         }
       }
     } else if (kFp8 && !kV8) {   // 16 keys -> bf16 chunks 2vc (keys 16vc ..) and 2vc + 1
-      const int key_rel = keys_of();
-      uint32_t keep_lo[4], keep_hi[4];
-      keep_mask(key_rel - vc * 16, keep_lo);
-      keep_mask(key_rel - vc * 16 - 8, keep_hi);
+      // Single-token slots: the key count is the same in every lane, so a
+      // scalar branch lets a tile wholly below the slot end -- every tile
+      // but a slot's last -- skip the masks (64 of the 96 VALU instructions
+      // of this step).  Token pairs keep one path: the branch cost their
+      // register allocation a spill.
+      const int key_rel = kTps == 1 ? readfirstlane(keys_of()) : keys_of();
+      if (kTps == 1 && key_rel >= kPage) {
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k) {
-        const intx4 c = st[k];
-        *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc)) = apply_keep(e4m3x8_to_bf16(c.x, c.y), keep_lo);
-        *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc + 1)) = apply_keep(e4m3x8_to_bf16(c.z, c.w), keep_hi);
+        for (int k = 0; k < kPerThread; ++k) {
+          const intx4 c = st[k];
+          *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc)) = e4m3x8_to_bf16(c.x, c.y);
+          *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc + 1)) = e4m3x8_to_bf16(c.z, c.w);
+        }
+      } else {
+        uint32_t keep_lo[4], keep_hi[4];
+        keep_mask(key_rel - vc * 16, keep_lo);
+        keep_mask(key_rel - vc * 16 - 8, keep_hi);
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+          const intx4 c = st[k];
+          *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc)) = apply_keep(e4m3x8_to_bf16(c.x, c.y), keep_lo);
+          *reinterpret_cast<intx4*>(vslot + vlds(k, 2 * vc + 1)) = apply_keep(e4m3x8_to_bf16(c.z, c.w), keep_hi);
+        }
       }
     } else {
       const int key_rel = keys_of();
