@@ -21,13 +21,14 @@ from gpu_helpers import assert_parity, to_device
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 @pytest.mark.parametrize("splits", [0, 3])
-def test_graph_replay_matches_eager_with_fresh_lengths(splits):
+def test_graph_replay_matches_eager_with_fresh_lengths(splits, kv):
     # The cache is drawn for the longest lengths of the schedule (rows past
     # those are NaN); the replays run with shorter or equal lengths.
     schedule = [[900, 64, 0, 2500, 1], [901, 65, 1, 2501, 2], [1000, 128, 64, 2560, 63]]
     case = make_decode_case(301, batch=5, ctx_lens=schedule[-1], hq=64, hkv=1, d=256,
-                            scale=1 / 16)
+                            kv_format=kv, scale=1 / 16)
     t = to_device(case)
     lens = t["lens"]
     lens.copy_(torch.tensor(schedule[0], dtype=torch.int32))
@@ -36,7 +37,7 @@ def test_graph_replay_matches_eager_with_fresh_lengths(splits):
 
     def call(out):
         mfa.mfa_decode_attention(t["q"], t["k"], t["v"], t["table"], lens, out, case.scale,
-                                 num_splits=splits)
+                                 k_scale=t["k_scale"], v_scale=t["v_scale"], num_splits=splits)
 
     call(out_e)                 # warm-up outside capture (allocates the workspace)
     torch.cuda.synchronize()
@@ -57,7 +58,7 @@ def test_graph_replay_matches_eager_with_fresh_lengths(splits):
         assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"replay {step}"
         ref = decode_attention(case.q, case.k_cache, case.v_cache, np.array(new_lens), case.scale,
                                **case.oracle_kwargs())
-        assert_parity(out_g, ref, "bf16", f"replay {step}")
+        assert_parity(out_g, ref, kv, f"replay {step}")
 
 
 def _replay_against_eager(call, outs_g, outs_e, before_each, steps):
