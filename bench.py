@@ -357,7 +357,7 @@ def main():
                          "context) and print its own line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the decode path shards by slot with no cross-GPU traffic, so run one "
               "process per GPU", file=sys.stderr)
         sys.exit(2)
