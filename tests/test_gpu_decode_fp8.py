@@ -132,6 +132,23 @@ def test_config4_full_size_every_slot():
     assert_parity(out, _every_slot_oracle(dc), "e4m3", "config 4", per_slot=True)
 
 
+def test_fp8_ragged_balanced_every_slot():
+    """The ragged continuous-batching shape (128 slots, prefill ~ U[1024,
+    8192] plus a geometric decode index) over an E4M3 cache drawn on the
+    device: the heuristic's balanced page cut (slots cut into pieces across
+    workgroups, single-token slots on the E4M3 S^T product) meets the bar on
+    every slot."""
+    from workloads import ragged_lengths
+    lens = ragged_lengths(128)(np.random.default_rng(33))
+    dc = make_device_case(33, batch=128, ctx_lens=lens, hq=64, hkv=1, d=256,
+                          kv_format="e4m3", scale=1 / 16, name="c3-fp8")
+    out = torch.full((128, 64, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mfa.mfa_decode_attention(dc.q, dc.k, dc.v, dc.table, dc.lens, out, dc.scale,
+                             k_scale=dc.k_scale, v_scale=dc.v_scale)
+    torch.cuda.synchronize()
+    assert_parity(out, _every_slot_oracle(dc), "e4m3", "ragged fp8", per_slot=True)
+
+
 def test_config4_query_path_into_fp8_attention_every_slot():
     """Config 4 as one chain: the low-rank query path (x [256, 7168] ->
     W_qdown -> RMSNorm -> W_qup -> 64 x 256, bf16 weights) feeds FP8-cache
