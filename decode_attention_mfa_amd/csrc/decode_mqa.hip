@@ -749,8 +749,12 @@ __global__ void __launch_bounds__(256 + kLoaders) mqa_decode_kernel(DecodeParams
         for (int ct = 0; ct < kD / 16; ++ct)
           __builtin_nontemporal_store(acc[tk][ct], reinterpret_cast<floatx4*>(p.part_o + row * kD + ct * 16 + id.q4 * 4));
       }
-      if (id.q4 == 0)
-        __builtin_nontemporal_store(floatx2{m_run[tk], l_tot}, reinterpret_cast<floatx2*>(p.part_ml + row * 2));
+      if (id.q4 == 0) {   // (m, l): cached for single tokens, streamed for pairs, as the rows
+        if constexpr (kTps == 1)
+          *reinterpret_cast<floatx2*>(p.part_ml + row * 2) = floatx2{m_run[tk], l_tot};
+        else
+          __builtin_nontemporal_store(floatx2{m_run[tk], l_tot}, reinterpret_cast<floatx2*>(p.part_ml + row * 2));
+      }
     }
   };
 
